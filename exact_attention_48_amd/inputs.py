@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the tests, the benchmark and the CPU reference: it
+draws random numbers and rounds them to bfloat16, and it holds none of the
+attention arithmetic.
+
+Recipe (the same for every workload):
+  * ``rng = numpy.random.default_rng(seed)``;
+  * for packed variable-length batches the sequence lengths are drawn first,
+    ``rng.integers(lo, hi, endpoint=True, size=n_seqs)``, and ``cu_seqlens`` is
+    ``[0, cumsum(lengths)]`` as int32;
+  * then ``rng.standard_normal(shape, dtype=float32)`` for Q, K, V and (for the
+    backward workload) dO, in that order;
+  * every float32 draw is rounded to bfloat16 with round-to-nearest-even.
+
+Tensor layouts ("BSHD", contiguous): Q/O/dO ``[B, N, Hq, d]``, K/V
+``[B, N, Hkv, d]``; packed: Q ``[T, Hq, d]``, K/V ``[T, Hkv, d]`` with
+``T = cu_seqlens[-1]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# bfloat16 <-> float32 bit conversions (round-to-nearest-even)
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, returning the uint16 bit patterns.
+
+    Round-to-nearest, ties to even, on the raw IEEE-754 bits; NaN stays a
+    quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float64."""
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Workload descriptions
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "fwd" or "bwd"
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    seed: int
+    B: int = 1           # batch size (uniform) or number of sequences (packed)
+    N: int = 0           # sequence length (uniform); max length (packed, set on draw)
+    varlen: bool = False
+    len_lo: int = 0      # packed: inclusive length range of the uniform draw
+    len_hi: int = 0
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), rounded to float32 (the value passed to the kernels)."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The five workloads (names say what they are).
+WORKLOADS = {
+    "fwd_b1_h2_n256_d64": Workload(
+        "fwd_b1_h2_n256_d64", "fwd", Hq=2, Hkv=2, d=64, causal=False, seed=1, B=1, N=256),
+    "fwd_b4_h16_n4096_d128": Workload(
+        "fwd_b4_h16_n4096_d128", "fwd", Hq=16, Hkv=16, d=128, causal=False, seed=2, B=4, N=4096),
+    "fwd_causal_b2_h16_n16384_d128": Workload(
+        "fwd_causal_b2_h16_n16384_d128", "fwd", Hq=16, Hkv=16, d=128, causal=True, seed=3, B=2, N=16384),
+    "fwd_causal_varlen16_hq32_hkv8_d128": Workload(
+        "fwd_causal_varlen16_hq32_hkv8_d128", "fwd", Hq=32, Hkv=8, d=128, causal=True, seed=4,
+        B=16, varlen=True, len_lo=512, len_hi=16384),
+    "bwd_causal_b2_h16_n8192_d128": Workload(
+        "bwd_causal_b2_h16_n8192_d128", "bwd", Hq=16, Hkv=16, d=128, causal=True, seed=5, B=2, N=8192),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    """bf16 bit patterns (uint16) for the operands, plus the packing metadata."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray]   # int32 [B+1] or None
+    B: int
+    N: int                             # uniform length, or max length when packed
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    scale: float
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1]) if self.cu_seqlens is not None else self.B * self.N
+
+    def lengths(self) -> np.ndarray:
+        if self.cu_seqlens is None:
+            return np.full(self.B, self.N, dtype=np.int64)
+        return np.diff(self.cu_seqlens.astype(np.int64))
+
+
+def _draw_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def draw_lengths(rng: np.random.Generator, n_seqs: int, lo: int, hi: int) -> np.ndarray:
+    return rng.integers(lo, hi, endpoint=True, size=n_seqs).astype(np.int64)
+
+
+def make_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, causal: bool, seed: int,
+                scale: Optional[float] = None, with_do: bool = False,
+                lengths: Optional[np.ndarray] = None, len_range: Optional[tuple] = None,
+                n_seqs: Optional[int] = None) -> Inputs:
+    """Draw one seeded input set.
+
+    Uniform batch: ``lengths`` and ``len_range`` are None, tensors are BSHD.
+    Packed batch: give explicit ``lengths`` or ``len_range=(lo, hi)`` with
+    ``n_seqs``; lengths are drawn first from the same generator.
+    """
+    rng = np.random.default_rng(seed)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    cu = None
+    if len_range is not None:
+        lengths = draw_lengths(rng, n_seqs, len_range[0], len_range[1])
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B = len(lengths)
+        N = int(lengths.max()) if len(lengths) else 0
+        T = int(cu[-1])
+        qs, ks = (T, Hq, d), (T, Hkv, d)
+    else:
+        qs, ks = (B, N, Hq, d), (B, N, Hkv, d)
+    q = _draw_bf16(rng, qs)
+    k = _draw_bf16(rng, ks)
+    v = _draw_bf16(rng, ks)
+    do = _draw_bf16(rng, qs) if with_do else None
+    return Inputs(q=q, k=k, v=v, do=do, cu_seqlens=cu, B=B, N=N, Hq=Hq, Hkv=Hkv, d=d,
+                  causal=causal, scale=scale)
+
+
+def workload_inputs(name: str) -> Inputs:
+    w = WORKLOADS[name]
+    if w.varlen:
+        return make_inputs(w.B, 0, w.Hq, w.Hkv, w.d, w.causal, w.seed, scale=w.scale,
+                           with_do=(w.kind == "bwd"), len_range=(w.len_lo, w.len_hi), n_seqs=w.B)
+    return make_inputs(w.B, w.N, w.Hq, w.Hkv, w.d, w.causal, w.seed, scale=w.scale,
+                       with_do=(w.kind == "bwd"))
+
+
+def counted_flops(lengths, Hq: int, d: int, causal: bool, backward: bool = False) -> float:
+    """Counted work: 4*Hq*d*sum(L^2), halved for causal; the backward counts 2.5x."""
+    s = float(np.sum(np.asarray(lengths, dtype=np.float64) ** 2))
+    f = 4.0 * Hq * d * s
+    if causal:
+        f *= 0.5
+    if backward:
+        f *= 2.5
+    return f

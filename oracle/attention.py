@@ -1,0 +1,180 @@
+"""CPU reference for exact softmax attention, in float64 (test infrastructure).
+
+This module is the oracle that the HIP kernels are checked against. It is
+test infrastructure only: the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import it; the library never does.
+
+What it computes is the plain definition of exact attention, the result that
+FlashAttention's tiling with an online softmax reaches without ever writing
+the N x N score matrix to memory ("FlashAttention-4 Conquers Asymmetric GPU
+Hardware Scaling", podcast.app episode page, second paragraph of the
+description; reference 2 there, "FlashAttention: Fast and Memory-Efficient
+Exact Attention with IO-Awareness"). Because the tiled method is exact, the
+oracle materialises S and P in full instead of tiling, and shares nothing
+with the GPU path.
+
+For one sequence of length L, one query head h and its key/value head
+g = h // (Hq // Hkv):
+  S[i, j] = scale * sum_k Q[i, h, k] K[j, g, k]; with causal masking
+            S[i, j] = -inf for j > i (positions local to the sequence)
+  m_i     = max_j S[i, j]
+  l_i     = sum_j exp(S[i, j] - m_i)
+  P[i, j] = exp(S[i, j] - m_i) / l_i
+  O[i]    = sum_j P[i, j] V[j, g]
+  LSE_i   = m_i + ln(l_i)          (natural log of sum_j exp(S[i, j]))
+Backward, for an upstream gradient dO (the backward pass named in the
+abstract on the zhuanzhiai.com page):
+  dV[j, g] = sum over heads h of group g, sum_i P[i, j] dO[i, h]
+  dP[i, j] = dO[i, h] . V[j, g]
+  D_i      = dO[i, h] . O[i, h]
+  dS[i, j] = P[i, j] (dP[i, j] - D_i)
+  dQ[i, h] = scale * sum_j dS[i, j] K[j, g]
+  dK[j, g] = scale * sum over heads h of group g, sum_i dS[i, j] Q[i, h]
+
+Layouts (contiguous "BSHD"): uniform batches Q/O/dO [B, N, Hq, d] and K/V
+[B, N, Hkv, d], LSE [B, Hq, N]; packed variable-length batches (the
+cu_seqlens form; the daily.dev summary names variable sequence lengths)
+Q [T, Hq, d], K/V [T, Hkv, d], LSE [Hq, T], sequence s occupying rows
+cu_seqlens[s] .. cu_seqlens[s+1]-1.
+
+Inputs are float64 arrays (the exact values of the bf16 operands).
+"""
+from __future__ import annotations
+
+from typing import Callable, Iterator, Optional, Tuple
+
+import numpy as np
+
+RowSelect = Optional[Callable[[int, int], np.ndarray]]
+
+
+def _segments(q: np.ndarray, cu_seqlens: Optional[np.ndarray]) -> Iterator[Tuple[int, slice, int]]:
+    """Yield (sequence index, token slice, length) for each sequence.
+
+    Uniform batches ([B, N, H, d]) yield batch indices with slice(None);
+    packed batches ([T, H, d]) yield row ranges of the packed tensor.
+    """
+    if cu_seqlens is None:
+        for b in range(q.shape[0]):
+            yield b, slice(None), q.shape[1]
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        for s in range(len(cu) - 1):
+            yield s, slice(int(cu[s]), int(cu[s + 1])), int(cu[s + 1] - cu[s])
+
+
+def _seq(x: np.ndarray, s: int, sl: slice, packed: bool) -> np.ndarray:
+    """The [L, H, d] block of sequence s."""
+    return x[sl] if packed else x[s]
+
+
+def head_scores(qh: np.ndarray, kh: np.ndarray, scale: float, causal: bool,
+                rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """S = scale * Q K^T for one head, with -inf above the diagonal when causal.
+
+    qh [L, d], kh [L, d]; ``rows`` (local query indices) restricts the rows.
+    """
+    if rows is None:
+        rows = np.arange(qh.shape[0])
+    s = scale * (qh[rows] @ kh.T)
+    if causal:
+        j = np.arange(kh.shape[0])
+        s[j[None, :] > rows[:, None]] = -np.inf
+    return s
+
+
+def head_forward(qh, kh, vh, scale, causal, rows=None):
+    """Softmax attention for one (sequence, head): returns (O [R, d], LSE [R], P [R, L])."""
+    s = head_scores(qh, kh, scale, causal, rows)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    p = e / l[:, None]
+    o = p @ vh
+    lse = m + np.log(l)
+    return o, lse, p
+
+
+def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                      causal: bool, cu_seqlens: Optional[np.ndarray] = None,
+                      rows: RowSelect = None):
+    """Exact attention forward. Returns (O, LSE) in float64.
+
+    ``rows(s, L)`` may return the local query rows of sequence s to compute;
+    rows not computed are NaN in the outputs (used for sampled checks of very
+    long sequences, where every computed row is still exact).
+    """
+    packed = cu_seqlens is not None
+    Hq, Hkv = q.shape[-2], k.shape[-2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    o = np.full(q.shape, np.nan, dtype=np.float64)
+    if packed:
+        lse = np.full((Hq, q.shape[0]), np.nan, dtype=np.float64)
+    else:
+        lse = np.full((q.shape[0], Hq, q.shape[1]), np.nan, dtype=np.float64)
+    for s, sl, L in _segments(q, cu_seqlens):
+        if L == 0:
+            continue
+        qs, ks, vs = _seq(q, s, sl, packed), _seq(k, s, sl, packed), _seq(v, s, sl, packed)
+        r = np.arange(L) if rows is None else np.asarray(rows(s, L), dtype=np.int64)
+        for h in range(Hq):
+            g = h // G
+            oh, lh, _ = head_forward(qs[:, h, :], ks[:, g, :], vs[:, g, :], scale, causal, r)
+            if packed:
+                o[sl.start + r, h, :] = oh
+                lse[h, sl.start + r] = lh
+            else:
+                o[s, r, h, :] = oh
+                lse[s, h, r] = lh
+    return o, lse
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                       scale: float, causal: bool, cu_seqlens: Optional[np.ndarray] = None):
+    """Gradients of the exact attention output. Returns (dQ, dK, dV) in float64.
+
+    O, P and D are the oracle's own float64 values, recomputed from Q, K, V.
+    """
+    packed = cu_seqlens is not None
+    Hq, Hkv = q.shape[-2], k.shape[-2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for s, sl, L in _segments(q, cu_seqlens):
+        if L == 0:
+            continue
+        qs, ks, vs = _seq(q, s, sl, packed), _seq(k, s, sl, packed), _seq(v, s, sl, packed)
+        dos = _seq(do, s, sl, packed)
+        dqs, dks, dvs = _seq(dq, s, sl, packed), _seq(dk, s, sl, packed), _seq(dv, s, sl, packed)
+        for h in range(Hq):
+            g = h // G
+            gq, gk, gv = head_backward(qs[:, h, :], ks[:, g, :], vs[:, g, :], dos[:, h, :], scale, causal)
+            dqs[:, h, :] += gq
+            dks[:, g, :] += gk
+            dvs[:, g, :] += gv
+    return dq, dk, dv
+
+
+def head_backward(qh, kh, vh, doh, scale, causal):
+    """Gradients for one (sequence, query head): returns (dQ [L, d], dK [L, d], dV [L, d])."""
+    oh, _, p = head_forward(qh, kh, vh, scale, causal)
+    dv = p.T @ doh
+    dp = doh @ vh.T
+    d_row = np.sum(doh * oh, axis=1)
+    ds = p * (dp - d_row[:, None])
+    dq = scale * (ds @ kh)
+    dk = scale * (ds.T @ qh)
+    return dq, dk, dv
+
+
+def backward_rowdot(do: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """D_i = sum_k dO[i, h, k] O[i, h, k], shaped like the LSE ([B, Hq, N] or [Hq, T])."""
+    d = np.sum(do * o, axis=-1)
+    if d.ndim == 3:
+        return np.transpose(d, (0, 2, 1)).copy()
+    return d.T.copy()

@@ -1,0 +1,322 @@
+"""Pins for the float64 attention oracle.
+
+Each ``pin_*`` function checks an attention implementation given as two
+callables,
+    fwd(q, k, v, scale, causal, cu_seqlens) -> (O, LSE)
+    bwd(q, k, v, do, scale, causal, cu_seqlens) -> (dQ, dK, dV)
+against something other than the implementation itself: brute force in pure
+Python, closed forms, invariants of softmax attention, reductions to simpler
+cases, a library routine (PyTorch's fp64 CPU attention and autograd) and
+central finite differences. The same functions are run against deliberately
+broken copies of the oracle to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from oracle import bruteforce
+
+TOL = 1e-11
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _cu(lengths):
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return cu
+
+
+# ---------------------------------------------------------------------------
+# brute force
+# ---------------------------------------------------------------------------
+
+BRUTE_CASES = [
+    # (B, N, Hq, Hkv, d, causal)
+    (1, 5, 1, 1, 3, False),
+    (2, 7, 2, 1, 4, True),
+    (1, 6, 4, 2, 8, False),
+    (1, 9, 4, 2, 5, True),
+    (2, 1, 2, 2, 3, True),
+]
+BRUTE_VARLEN = [([1, 3, 5], 4, 2, 6, True), ([4, 2, 7], 2, 1, 3, False)]
+
+
+def pin_bruteforce(fwd, bwd=None):
+    rng = np.random.default_rng(11)
+    for (B, N, Hq, Hkv, d, causal) in BRUTE_CASES:
+        q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, d)
+        scale = 0.37
+        o, lse = fwd(q, k, v, scale, causal, None)
+        ob, lb = bruteforce.forward(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+        assert np.max(np.abs(o - np.array(ob))) < TOL, ("O vs brute force", B, N, Hq, Hkv, d, causal)
+        assert np.max(np.abs(lse - np.array(lb))) < TOL, ("LSE vs brute force", B, N, Hq, Hkv, d, causal)
+    for (lens, Hq, Hkv, d, causal) in BRUTE_VARLEN:
+        cu = _cu(lens)
+        T = int(cu[-1])
+        q, k, v = _rand(rng, T, Hq, d), _rand(rng, T, Hkv, d), _rand(rng, T, Hkv, d)
+        o, lse = fwd(q, k, v, 0.5, causal, cu)
+        ob, lb = bruteforce.forward(q.tolist(), k.tolist(), v.tolist(), 0.5, causal, cu.tolist())
+        assert np.max(np.abs(o - np.array(ob))) < TOL, ("varlen O vs brute force", lens)
+        assert np.max(np.abs(lse - np.array(lb))) < TOL, ("varlen LSE vs brute force", lens)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def pin_closed_forms(fwd, bwd=None):
+    rng = np.random.default_rng(12)
+    # one key: O = V_0 and LSE = scale * q0.k0
+    q, k, v = _rand(rng, 3, 1, 2, 4), _rand(rng, 3, 1, 2, 4), _rand(rng, 3, 1, 2, 4)
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, 0.3, causal, None)
+        assert np.allclose(o, v, atol=TOL, rtol=0), "single key must return V_0"
+        want = 0.3 * np.einsum("bnhd,bnhd->bhn", q, k)
+        assert np.allclose(lse, want, atol=TOL, rtol=0), "single-key LSE"
+    # identical V rows: O equals that row for every query
+    B, N, H, d = 2, 6, 2, 5
+    q, k = _rand(rng, B, N, H, d), _rand(rng, B, N, H, d)
+    row = _rand(rng, B, 1, H, d)
+    v = np.repeat(row, N, axis=1)
+    for causal in (False, True):
+        o, _ = fwd(q, k, v, 0.7, causal, None)
+        assert np.allclose(o, np.repeat(row, N, axis=1), atol=TOL, rtol=0), "identical V rows"
+    # all-ones V: each softmax row sums to one
+    v1 = np.ones((B, N, H, d))
+    o, _ = fwd(q, k, v1, 0.7, True, None)
+    assert np.allclose(o, 1.0, atol=TOL, rtol=0), "softmax rows must sum to 1"
+    # causal row 0: O_0 = V_0 and LSE_0 = scale * q0.k0
+    v = _rand(rng, B, N, H, d)
+    o, lse = fwd(q, k, v, 0.7, True, None)
+    assert np.allclose(o[:, 0], v[:, 0], atol=TOL, rtol=0), "causal first row equals V_0"
+    assert np.allclose(lse[:, :, 0], 0.7 * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]), atol=TOL, rtol=0)
+    # Q = 0: uniform weights over the visible keys
+    qz = np.zeros_like(q)
+    for causal in (False, True):
+        o, lse = fwd(qz, k, v, 0.7, causal, None)
+        for i in range(N):
+            vis = i + 1 if causal else N
+            assert np.allclose(o[:, i], v[:, :vis].mean(axis=1), atol=TOL, rtol=0), "Q=0 gives the mean of V"
+            assert np.allclose(lse[:, :, i], math.log(vis), atol=TOL, rtol=0), "Q=0 gives LSE = ln(#keys)"
+    # two keys, scalar head: O = logistic(a), LSE = ln(1 + e^a)
+    for a in (-3.0, -0.25, 0.0, 1.5, 7.0):
+        q2 = np.array([[[[a]], [[0.0]]]])        # [1, 2, 1, 1]; row 1 unused
+        k2 = np.array([[[[0.0]], [[1.0]]]])
+        v2 = np.array([[[[0.0]], [[1.0]]]])
+        o, lse = fwd(q2, k2, v2, 1.0, False, None)
+        assert abs(o[0, 0, 0, 0] - 1.0 / (1.0 + math.exp(-a))) < TOL, "two-key logistic"
+        assert abs(lse[0, 0, 0] - math.log1p(math.exp(a))) < TOL, "two-key LSE"
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def pin_invariants(fwd, bwd=None):
+    rng = np.random.default_rng(13)
+    B, N, Hq, Hkv, d = 2, 9, 4, 2, 6
+    G = Hq // Hkv
+    q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, d)
+    scale = 0.45
+    for causal in (False, True):
+        o, lse = fwd(q, k, v, scale, causal, None)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G
+                for i in range(N):
+                    vis = i + 1 if causal else N
+                    vv = v[b, :vis, g]
+                    assert np.all(o[b, i, h] >= vv.min(axis=0) - TOL) and np.all(o[b, i, h] <= vv.max(axis=0) + TOL), \
+                        "O must lie in the per-column range of the visible V rows"
+                    smax = max(scale * float(np.dot(q[b, i, h], k[b, j, g])) for j in range(vis))
+                    assert smax - TOL <= lse[b, h, i] <= smax + math.log(vis) + TOL, "max S <= LSE <= max S + ln(#keys)"
+        # translating every key by u leaves O unchanged and shifts LSE by scale q.u
+        u = _rand(rng, d)
+        o2, lse2 = fwd(q, k + u, v, scale, causal, None)
+        assert np.allclose(o2, o, atol=1e-10, rtol=0), "key translation changes O"
+        shift = scale * np.einsum("bnhd,d->bhn", q, u)
+        assert np.allclose(lse2, lse + shift, atol=1e-10, rtol=0), "key translation must shift LSE by scale*q.u"
+        # adding c to every V entry adds c to O
+        o3, lse3 = fwd(q, k, v + 2.5, scale, causal, None)
+        assert np.allclose(o3, o + 2.5, atol=1e-10, rtol=0) and np.allclose(lse3, lse, atol=TOL, rtol=0)
+    # joint permutation of keys and values (non-causal) leaves O and LSE unchanged
+    o, lse = fwd(q, k, v, scale, False, None)
+    perm = rng.permutation(N)
+    o4, lse4 = fwd(q, k[:, perm], v[:, perm], scale, False, None)
+    assert np.allclose(o4, o, atol=1e-12, rtol=0) and np.allclose(lse4, lse, atol=1e-12, rtol=0)
+    # doubling scale equals doubling Q
+    o5, lse5 = fwd(q, k, v, 2 * scale, True, None)
+    o6, lse6 = fwd(2 * q, k, v, scale, True, None)
+    assert np.allclose(o5, o6, atol=1e-12, rtol=0) and np.allclose(lse5, lse6, atol=1e-12, rtol=0)
+
+
+def pin_logsumexp(fwd, bwd=None):
+    """LSE equals a direct, correctly rounded log-sum-exp of the scaled scores."""
+    rng = np.random.default_rng(14)
+    B, N, H, d = 1, 8, 2, 4
+    q, k, v = _rand(rng, B, N, H, d) * 3, _rand(rng, B, N, H, d), _rand(rng, B, N, H, d)
+    for causal in (False, True):
+        _, lse = fwd(q, k, v, 0.8, causal, None)
+        for h in range(H):
+            for i in range(N):
+                vis = i + 1 if causal else N
+                sc = [0.8 * math.fsum(a * b for a, b in zip(q[0, i, h], k[0, j, h])) for j in range(vis)]
+                assert abs(lse[0, h, i] - bruteforce.logsumexp_direct(sc)) < TOL
+
+
+# ---------------------------------------------------------------------------
+# reductions
+# ---------------------------------------------------------------------------
+
+def pin_reductions(fwd, bwd=None):
+    rng = np.random.default_rng(15)
+    B, N, Hq, Hkv, d = 2, 10, 6, 2, 4
+    G = Hq // Hkv
+    q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, d)
+    do = _rand(rng, B, N, Hq, d)
+    for causal in (False, True):
+        # grouped heads == multi-head attention with each K/V head repeated G times
+        o, lse = fwd(q, k, v, 0.6, causal, None)
+        kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+        o2, lse2 = fwd(q, kr, vr, 0.6, causal, None)
+        assert np.allclose(o, o2, atol=1e-12, rtol=0) and np.allclose(lse, lse2, atol=1e-12, rtol=0), "GQA reduction"
+        if bwd is not None:
+            dq, dk, dv = bwd(q, k, v, do, 0.6, causal, None)
+            dq2, dkr, dvr = bwd(q, kr, vr, do, 0.6, causal, None)
+            assert np.allclose(dq, dq2, atol=1e-11, rtol=0), "GQA dQ reduction"
+            assert np.allclose(dk, dkr.reshape(B, N, Hkv, G, d).sum(axis=3), atol=1e-11, rtol=0), "GQA dK group sum"
+            assert np.allclose(dv, dvr.reshape(B, N, Hkv, G, d).sum(axis=3), atol=1e-11, rtol=0), "GQA dV group sum"
+        # causal row i == non-causal attention of q_i over keys 0..i
+        if causal:
+            for i in (0, 3, N - 1):
+                # attention of query i over keys 0..i, as a non-causal call
+                # (the query is repeated to fill the i+1 query rows)
+                qq = np.concatenate([q[:, i:i + 1]] * (i + 1), axis=1)
+                oi, li = fwd(qq, k[:, :i + 1], v[:, :i + 1], 0.6, False, None)
+                assert np.allclose(oi[:, 0], o[:, i], atol=1e-12, rtol=0), "causal row reduction (O)"
+                assert np.allclose(li[:, :, 0], lse[:, :, i], atol=1e-12, rtol=0), "causal row reduction (LSE)"
+    # packed variable length == separate uniform calls per sequence
+    lens = [3, 1, 7, 5]
+    cu = _cu(lens)
+    T = int(cu[-1])
+    qp, kp, vp = _rand(rng, T, Hq, d), _rand(rng, T, Hkv, d), _rand(rng, T, Hkv, d)
+    dop = _rand(rng, T, Hq, d)
+    for causal in (False, True):
+        o, lse = fwd(qp, kp, vp, 0.6, causal, cu)
+        grads = bwd(qp, kp, vp, dop, 0.6, causal, cu) if bwd is not None else None
+        for s, L in enumerate(lens):
+            a, b = int(cu[s]), int(cu[s + 1])
+            os_, ls_ = fwd(qp[None, a:b], kp[None, a:b], vp[None, a:b], 0.6, causal, None)
+            assert np.allclose(o[a:b], os_[0], atol=1e-12, rtol=0), "varlen O reduction"
+            assert np.allclose(lse[:, a:b], ls_[0], atol=1e-12, rtol=0), "varlen LSE reduction"
+            if grads is not None:
+                gs = bwd(qp[None, a:b], kp[None, a:b], vp[None, a:b], dop[None, a:b], 0.6, causal, None)
+                for x, y in zip(grads, gs):
+                    assert np.allclose(x[a:b], y[0], atol=1e-11, rtol=0), "varlen gradient reduction"
+
+
+# ---------------------------------------------------------------------------
+# library cross-check (PyTorch CPU float64)
+# ---------------------------------------------------------------------------
+
+def _torch_reference(q, k, v, do, scale, causal):
+    import torch
+    Hq, Hkv = q.shape[2], k.shape[2]
+    G = Hq // Hkv
+    tq = torch.tensor(q, dtype=torch.float64).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tk = torch.tensor(k, dtype=torch.float64).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tv = torch.tensor(v, dtype=torch.float64).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    kr = tk.repeat_interleave(G, dim=1)
+    vr = tv.repeat_interleave(G, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, kr, vr, is_causal=causal, scale=scale)
+    s = torch.matmul(tq, kr.transpose(-1, -2)) * scale
+    if causal:
+        N = q.shape[1]
+        mask = torch.ones(N, N, dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    tdo = torch.tensor(do, dtype=torch.float64).permute(0, 2, 1, 3)
+    gq, gk, gv = torch.autograd.grad(out, (tq, tk, tv), tdo)
+    t = lambda x: x.detach().permute(0, 2, 1, 3).numpy()
+    return t(out), lse.detach().numpy(), t(gq), t(gk), t(gv)
+
+
+def pin_torch(fwd, bwd=None):
+    rng = np.random.default_rng(16)
+    for (B, N, Hq, Hkv, d, causal) in [(2, 33, 4, 2, 16, True), (1, 40, 2, 2, 8, False), (1, 17, 8, 1, 32, True)]:
+        q, k, v = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, d)
+        do = _rand(rng, B, N, Hq, d)
+        o_t, lse_t, dq_t, dk_t, dv_t = _torch_reference(q, k, v, do, 0.3, causal)
+        o, lse = fwd(q, k, v, 0.3, causal, None)
+        assert np.allclose(o, o_t, atol=1e-12, rtol=0), "O vs torch fp64"
+        assert np.allclose(lse, lse_t, atol=1e-12, rtol=0), "LSE vs torch fp64"
+        if bwd is not None:
+            dq, dk, dv = bwd(q, k, v, do, 0.3, causal, None)
+            assert np.allclose(dq, dq_t, atol=1e-11, rtol=0), "dQ vs torch autograd"
+            assert np.allclose(dk, dk_t, atol=1e-11, rtol=0), "dK vs torch autograd"
+            assert np.allclose(dv, dv_t, atol=1e-11, rtol=0), "dV vs torch autograd"
+
+
+# ---------------------------------------------------------------------------
+# backward: finite differences and gradient invariants
+# ---------------------------------------------------------------------------
+
+def pin_finite_differences(fwd, bwd):
+    """Central differences of L = sum(dO * O) match the analytic gradients."""
+    rng = np.random.default_rng(17)
+    cases = [((1, 5, 2, 1, 3), True, None), ((1, 4, 2, 2, 3), False, None)]
+    lens = [2, 4]
+    cases.append(((sum(lens), 2, 1, 3), True, _cu(lens)))
+    h = 1e-6
+    for shape, causal, cu in cases:
+        if cu is None:
+            B, N, Hq, Hkv, d = shape
+            qs, ks = (B, N, Hq, d), (B, N, Hkv, d)
+        else:
+            T, Hq, Hkv, d = shape
+            qs, ks = (T, Hq, d), (T, Hkv, d)
+        q, k, v, do = _rand(rng, *qs), _rand(rng, *ks), _rand(rng, *ks), _rand(rng, *qs)
+        scale = 0.55
+        grads = bwd(q, k, v, do, scale, causal, cu)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(do * fwd(qq, kk, vv, scale, causal, cu)[0]))
+
+        for which, x in enumerate((q, k, v)):
+            g = grads[which]
+            num = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                args_p = [q.copy(), k.copy(), v.copy()]
+                args_m = [q.copy(), k.copy(), v.copy()]
+                args_p[which][idx] += h
+                args_m[which][idx] -= h
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            err = np.max(np.abs(num - g)) / max(np.max(np.abs(num)), 1e-12)
+            assert err < 1e-6, ("finite differences", "QKV"[which], shape, causal, err)
+
+
+def pin_gradient_invariants(fwd, bwd):
+    """sum_j dK_j = 0 and sum_j dV_j = sum over the group's heads and rows of dO."""
+    rng = np.random.default_rng(18)
+    B, N, Hq, Hkv, d = 2, 12, 4, 2, 5
+    G = Hq // Hkv
+    q, k, v, do = _rand(rng, B, N, Hq, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hkv, d), _rand(rng, B, N, Hq, d)
+    for causal in (False, True):
+        dq, dk, dv = bwd(q, k, v, do, 0.4, causal, None)
+        assert np.allclose(dk.sum(axis=1), 0.0, atol=1e-11), "sum of dK over keys must vanish"
+        want = do.reshape(B, N, Hkv, G, d).sum(axis=(1, 3))
+        assert np.allclose(dv.sum(axis=1), want, atol=1e-11), "sum of dV over keys must equal sum of dO"
+        # V -> V + c leaves dQ and dK unchanged (softmax is shift-free in V's direction)
+        dq2, dk2, dv2 = bwd(q, k, v + 1.75, do, 0.4, causal, None)
+        assert np.allclose(dq2, dq, atol=1e-11) and np.allclose(dk2, dk, atol=1e-11) and np.allclose(dv2, dv, atol=1e-11)
+
+
+ALL_FWD_PINS = [pin_bruteforce, pin_closed_forms, pin_invariants, pin_logsumexp, pin_reductions, pin_torch]
+ALL_BWD_PINS = [pin_finite_differences, pin_gradient_invariants, pin_reductions, pin_torch]

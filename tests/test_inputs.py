@@ -1,0 +1,63 @@
+"""The seeded input recipe and the bf16 rounding it uses (CPU only)."""
+import numpy as np
+import torch
+
+from exact_attention_48_amd import inputs as I
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-39).astype(np.float32),          # subnormals
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.0e38, -3.0e38, 1.0 + 2**-8, 1.0 + 3 * 2**-8,
+                  1.0 + 2**-8 + 2**-20], dtype=np.float32),             # ties to even and just above
+    ])
+    ours = I.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+    back = I.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_nan_stays_nan():
+    b = I.f32_to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(I.bf16_bits_to_f32(b)[0])
+
+
+def test_uniform_inputs_are_seeded_and_shaped():
+    a = I.make_inputs(2, 5, 4, 2, 8, True, seed=7, with_do=True)
+    b = I.make_inputs(2, 5, 4, 2, 8, True, seed=7, with_do=True)
+    assert a.q.shape == (2, 5, 4, 8) and a.k.shape == (2, 5, 2, 8) and a.do.shape == (2, 5, 4, 8)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v), (a.do, b.do)):
+        assert x.dtype == np.uint16 and np.array_equal(x, y)
+    # the draw order is Q, K, V, dO from one generator
+    rng = np.random.default_rng(7)
+    q = I.f32_to_bf16_bits(rng.standard_normal((2, 5, 4, 8), dtype=np.float32))
+    assert np.array_equal(q, a.q)
+
+
+def test_packed_lengths_drawn_first():
+    w = I.WORKLOADS["fwd_causal_varlen16_hq32_hkv8_d128"]
+    rng = np.random.default_rng(w.seed)
+    lens = I.draw_lengths(rng, w.B, w.len_lo, w.len_hi)
+    assert len(lens) == 16 and lens.min() >= 512 and lens.max() <= 16384
+    small = I.make_inputs(0, 0, 2, 1, 8, True, seed=w.seed, len_range=(3, 9), n_seqs=5)
+    rng = np.random.default_rng(w.seed)
+    l2 = I.draw_lengths(rng, 5, 3, 9)
+    assert np.array_equal(np.diff(small.cu_seqlens), l2)
+    assert small.cu_seqlens.dtype == np.int32 and small.cu_seqlens[0] == 0
+    assert small.q.shape == (int(l2.sum()), 2, 8) and small.N == int(l2.max())
+
+
+def test_counted_flops():
+    assert I.counted_flops([4096] * 4, 16, 128, False) == 4 * 4 * 16 * 4096**2 * 128
+    assert abs(I.counted_flops([4096] * 4, 16, 128, False) - 5.498e11) / 5.498e11 < 1e-3
+    assert abs(I.counted_flops([16384] * 2, 16, 128, True) - 2.199e12) / 2.199e12 < 1e-3
+    assert abs(I.counted_flops([8192] * 2, 16, 128, True, backward=True) - 1.3744e12) / 1.3744e12 < 1e-3
+
+
+def test_scale_is_float32_rounded():
+    assert I.WORKLOADS["fwd_b1_h2_n256_d64"].scale == 0.125
+    s = I.WORKLOADS["fwd_b4_h16_n4096_d128"].scale
+    assert s == float(np.float32(1 / np.sqrt(128)))

@@ -1,0 +1,72 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is the oracle's own source with one plausible mistake edited in
+(a dropped term, a wrong sign, index or axis, a transposed operand); the pins
+in ``tests/oracle_pins.py`` must reject every one of them.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.attention as ref
+from tests import oracle_pins as pins
+
+SRC = inspect.getsource(ref)
+
+FWD_MUTANTS = {
+    "dropped_scale": ("s = scale * (qh[rows] @ kh.T)", "s = (qh[rows] @ kh.T)"),
+    "mask_includes_diagonal": ("s[j[None, :] > rows[:, None]] = -np.inf", "s[j[None, :] >= rows[:, None]] = -np.inf"),
+    "mask_wrong_side": ("s[j[None, :] > rows[:, None]] = -np.inf", "s[j[None, :] < rows[:, None]] = -np.inf"),
+    "q_k_swapped": ("s = scale * (qh[rows] @ kh.T)", "s = scale * (kh[rows] @ qh.T)"),
+    "lse_drops_max": ("lse = m + np.log(l)", "lse = np.log(l)"),
+    "lse_log2": ("lse = m + np.log(l)", "lse = m + np.log2(l)"),
+    "unnormalised_p": ("p = e / l[:, None]", "p = e"),
+    "normalised_wrong_axis": ("p = e / l[:, None]", "p = e / e.sum(axis=0)[None, :]"),
+    "gqa_modulo_mapping": ("g = h // G\n            oh, lh", "g = h % Hkv\n            oh, lh"),
+    "packed_lse_offset": ("lse[h, sl.start + r] = lh", "lse[h, r] = lh"),
+    "exp_sign": ("e = np.exp(s - m[:, None])", "e = np.exp(m[:, None] - s)"),
+}
+
+BWD_MUTANTS = {
+    "ds_sign_of_d": ("ds = p * (dp - d_row[:, None])", "ds = p * (dp + d_row[:, None])"),
+    "d_uses_do_twice": ("d_row = np.sum(doh * oh, axis=1)", "d_row = np.sum(doh * doh, axis=1)"),
+    "dq_drops_scale": ("dq = scale * (ds @ kh)", "dq = (ds @ kh)"),
+    "dk_untransposed": ("dk = scale * (ds.T @ qh)", "dk = scale * (ds @ qh)"),
+    "dv_untransposed": ("dv = p.T @ doh", "dv = p @ doh"),
+    "dp_extra_scale": ("dp = doh @ vh.T", "dp = scale * (doh @ vh.T)"),
+    "dk_group_overwrites": ("dks[:, g, :] += gk", "dks[:, g, :] = gk"),
+    "dv_group_overwrites": ("dvs[:, g, :] += gv", "dvs[:, g, :] = gv"),
+    "dq_uses_v": ("dq = scale * (ds @ kh)", "dq = scale * (ds @ vh)"),
+}
+
+
+def _mutant(old, new):
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    fwd = lambda q, k, v, scale, causal, cu: mod.attention_forward(q, k, v, scale, causal, cu)
+    bwd = lambda q, k, v, do, scale, causal, cu: mod.attention_backward(q, k, v, do, scale, causal, cu)
+    return fwd, bwd
+
+
+def _caught(pin_list, fwd, bwd):
+    for pin in pin_list:
+        try:
+            pin(fwd, bwd)
+        except Exception:
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(FWD_MUTANTS))
+def test_forward_mutant_is_caught(name):
+    fwd, bwd = _mutant(*FWD_MUTANTS[name])
+    assert _caught(pins.ALL_FWD_PINS, fwd, bwd) is not None, f"mutant {name} passed every forward pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    fwd, bwd = _mutant(*BWD_MUTANTS[name])
+    order = [pins.pin_gradient_invariants, pins.pin_torch, pins.pin_reductions, pins.pin_finite_differences]
+    assert _caught(order, fwd, bwd) is not None, f"mutant {name} passed every backward pin"
