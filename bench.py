@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one forward (fa_fwd) and one backward (fa_bwd: D pre-pass, dK/dV
+kernel, dQ kernel) over one batch of the B=4, Hq=Hkv=16, N=4096, d=128,
+non-causal workload, inputs resident in HBM. Counted work per step follows
+the FLOP convention of the metric: 4*B*Hq*N^2*d for the forward (halved for
+causal) and 2.5x that for the backward.
+
+Prints ONE JSON line with the step throughput (TFLOP/s), the roofline of the
+dominant kernel (timed live with HIP events on its launch stream), per-kernel
+and per-workload figures, and the float64 CPU oracle timed on a bounded sample
+on this machine's host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--main-only]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz (AMD: "2.5 PFLOP/s" dense BF16)
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X (% of dense BF16 MFMA peak)"
+MAIN = "fwd_b4_h16_n4096_d128"
+
+# Algorithmic work of each kernel per unmasked score element, in units of d FLOP:
+# forward: S = QK^T and O = PV (4d); dK/dV kernel: S, dP, dV, dK (8d); dQ kernel:
+# the dQ product only (2d; its S and dP recomputations are not algorithmic).
+KERNEL_FLOP_PER_ELEM = {"fa_fwd_kernel": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2, "bwd_dsum_kernel": 0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--main-only", action="store_true", help="skip the per-workload figures")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_48_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_kernels.h"],
+    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h"],
+    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h"],
+    "bwd_dsum_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h"],
+}
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_attention_48_amd import capi, inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    capi.load()
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- main workload: one step = fa_fwd + fa_bwd ----------------
+    w = I.WORKLOADS[MAIN]
+    x = I.make_inputs(w.B, w.N, w.Hq, w.Hkv, w.d, w.causal, w.seed, scale=w.scale, with_do=True)
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    B, N, Hq, Hkv, d, causal, scale = x.B, x.N, x.Hq, x.Hkv, x.d, int(x.causal), x.scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = capi.fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch_all(evs=None):
+        if evs: evs[0].record(stream)
+        capi.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, None, stream)
+        if evs: evs[1].record(stream)
+        capi.fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, None, ws, ws_bytes,
+                       capi.FA_BWD_PREPROCESS, stream)
+        if evs: evs[2].record(stream)
+        capi.fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, None, ws, ws_bytes,
+                       capi.FA_BWD_DKDV, stream)
+        if evs: evs[3].record(stream)
+        capi.fa_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, None, ws, ws_bytes,
+                       capi.FA_BWD_DQ, stream)
+        if evs: evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        launch_all()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        launch_all(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    names = ["fa_fwd_kernel", "bwd_dsum_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all(), "non-finite outputs"
+
+    lengths = [N] * B
+    f_fwd = I.counted_flops(lengths, Hq, d, bool(causal))
+    f_bwd = I.counted_flops(lengths, Hq, d, bool(causal), backward=True)
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    elems = B * Hq * float(N) * N * (0.5 if causal else 1.0)
+
+    kernels = {}
+    for n in names:
+        fl = KERNEL_FLOP_PER_ELEM[n] * d * elems
+        ent = {"ms": round(kms[n], 4)}
+        if fl > 0:
+            tf = fl / (kms[n] * 1e-3) / 1e12
+            ent.update({"algorithmic_tflop": round(fl / 1e12, 4), "tflops": round(tf, 1),
+                        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        else:
+            by = B * N * Hq * (2 * d * 2 + 4)
+            ent.update({"algorithmic_bytes": by, "gbs": round(by / (kms[n] * 1e-3) / 1e9, 1)})
+        kernels[n] = ent
+    dom = max(names, key=lambda n: kms[n])
+    dom_fl = KERNEL_FLOP_PER_ELEM[dom] * d * elems
+    achieved = dom_fl / (kms[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(dom, MAIN)}
+
+    # ---------------- per-workload figures (parity-test shapes) ----------------
+    workloads = {}
+    if not args.main_only:
+        g = torch.Generator(device=dev)
+
+        def rnd(shape, seed):
+            g.manual_seed(seed)
+            return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+        def time_it(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
+                     "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64"):
+            wl = I.WORKLOADS[name]
+            if wl.varlen:
+                lens = I.draw_lengths(np.random.default_rng(wl.seed), wl.B, wl.len_lo, wl.len_hi)
+                cu_h = np.zeros(len(lens) + 1, dtype=np.int32)
+                cu_h[1:] = np.cumsum(lens)
+                T, Nw = int(cu_h[-1]), int(lens.max())
+                qs, ks = (T, wl.Hq, wl.d), (T, wl.Hkv, wl.d)
+                cu = torch.from_numpy(cu_h).to(dev)
+                lse_w = torch.empty((wl.Hq, T), dtype=torch.float32, device=dev)
+            else:
+                lens = np.full(wl.B, wl.N)
+                Nw = wl.N
+                qs, ks = (wl.B, wl.N, wl.Hq, wl.d), (wl.B, wl.N, wl.Hkv, wl.d)
+                cu = None
+                lse_w = torch.empty((wl.B, wl.Hq, wl.N), dtype=torch.float32, device=dev)
+            qw, kw, vw = rnd(qs, wl.seed * 10 + 1), rnd(ks, wl.seed * 10 + 2), rnd(ks, wl.seed * 10 + 3)
+            ow = torch.empty_like(qw)
+            fwd = lambda: capi.fa_fwd(qw, kw, vw, ow, lse_w, wl.B, wl.Hq, wl.Hkv, Nw, wl.d, int(wl.causal),
+                                      wl.scale, cu, stream)
+            ent = {}
+            ms_f = time_it(fwd, 5 if Nw >= 8192 else 20)
+            fl = I.counted_flops(lens, wl.Hq, wl.d, wl.causal)
+            ent["fwd_ms"] = round(ms_f, 4)
+            ent["fwd_tflops"] = round(fl / (ms_f * 1e-3) / 1e12, 1)
+            ent["fwd_frac_of_peak"] = round(fl / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            if wl.kind == "bwd":
+                dow = rnd(qs, wl.seed * 10 + 4)
+                dqw, dkw, dvw = torch.empty_like(qw), torch.empty_like(kw), torch.empty_like(vw)
+                wsb = capi.fa_bwd_workspace_size(wl.B, wl.Hq, wl.Hkv, Nw, wl.d, int(wl.causal), int(wl.varlen))
+                wsw = torch.empty(wsb, dtype=torch.uint8, device=dev)
+                bwd = lambda: capi.fa_bwd(qw, kw, vw, ow, lse_w, dow, dqw, dkw, dvw, wl.B, wl.Hq, wl.Hkv, Nw, wl.d,
+                                          int(wl.causal), wl.scale, cu, wsw, wsb, stream)
+                ms_b = time_it(bwd, 5)
+                flb = I.counted_flops(lens, wl.Hq, wl.d, wl.causal, backward=True)
+                ent["bwd_ms"] = round(ms_b, 4)
+                ent["bwd_tflops"] = round(flb / (ms_b * 1e-3) / 1e12, 1)
+                ent["bwd_frac_of_peak"] = round(flb / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                del dow, dqw, dkw, dvw, wsw
+            workloads[name] = ent
+            del qw, kw, vw, ow, lse_w
+            torch.cuda.empty_cache()
+
+    # ---------------- CPU oracle baseline (bounded sample) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas = [t for t in threadpool_info() if t.get("user_api") == "blas"]
+            cores = int(blas[0]["num_threads"]) if blas else os.cpu_count()
+        except Exception:
+            cores = os.cpu_count()
+        n_heads = args.cpu_heads or 16
+        f64 = I.bf16_bits_to_f64
+        qh, kh, vh, doh = (f64(t[0:1, :, :n_heads]) for t in (x.q, x.k, x.v, x.do))
+        c0 = time.perf_counter()
+        oracle.attention_forward(qh, kh, vh, scale, bool(causal))
+        oracle.attention_backward(qh, kh, vh, doh, scale, bool(causal))
+        secs = time.perf_counter() - c0
+        fl = I.counted_flops([N], n_heads, d, bool(causal)) + I.counted_flops([N], n_heads, d, bool(causal), True)
+        cpu = {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "seconds": round(secs, 2),
+               "sample": f"float64 NumPy oracle, forward + backward of {n_heads} of the {B * Hq} (batch, head) "
+                         f"pairs of the same workload (N={N}, d={d}), counted FLOP / wall time"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"attention forward + backward, B={B}, Hq={Hq}, Hkv={Hkv}, N={N}, d={d}, "
+                               f"{'causal' if causal else 'non-causal'} (seeded N(0,1) bf16 inputs)",
+                   "global_batch": B, "seq_len": N, "heads_q": Hq, "heads_kv": Hkv, "head_dim": d,
+                   "causal": bool(causal), "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "workloads": workloads,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

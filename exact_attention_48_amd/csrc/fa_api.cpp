@@ -1,0 +1,129 @@
+// fa_api.cpp -- the C ABI (include/fa.h): validate, pick the kernel variant, launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+#include "fa_validate.h"
+
+namespace {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kDefaultTau = 8.0f;
+
+inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace fa {
+
+size_t bwd_workspace_bytes(long B, long Hq, long Hkv, long N, int d, int causal, int varlen) {
+  (void)Hkv;
+  (void)causal;
+  (void)varlen;
+  if (B <= 0 || N <= 0 || Hq <= 0) return 0;
+  (void)d;
+  const size_t rows = (size_t)B * (size_t)N;          // >= T for packed batches
+  return round256(rows * (size_t)Hq * sizeof(float)); // D_i, laid out like the LSE
+}
+
+}  // namespace fa
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid but not supported (head size or problem size)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_version(void) { return "fa-mi355x 0.1 (gfx950)"; }
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                    const int32_t* cu_seqlens, const fa_fwd_options* options, void* stream) {
+  const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
+  fa_status st = fa::check_fwd(q, k, v, o, lse, pr, softmax_scale, cu_seqlens, options);
+  if (st != FA_OK) return st;
+  if (fa::empty_problem(pr)) return FA_OK;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.N = N;
+  p.lpt = options ? options->lpt_order : 1;
+  p.xcd_group = p.G;
+  p.scale_log2 = softmax_scale * kLog2eF;
+  p.tau = options ? options->rescale_tau : kDefaultTau;
+  const int expmode = options ? options->exp_mode : FA_EXP_HW;
+  hipError_t e = fa::fwd_launch(p, d, causal, cu_seqlens != nullptr, expmode, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                 const int32_t* cu_seqlens, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, nullptr, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int varlen) {
+  return fa::bwd_workspace_bytes(B, Hq, Hkv, N, d, causal, varlen);
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                    const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, int stages,
+                    void* stream) {
+  if (stages < 1 || stages > FA_BWD_ALL) return FA_ERR_INVALID_ARGUMENT;
+  const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
+  const size_t needed = fa::bwd_workspace_bytes(B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr);
+  fa_status st = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, pr, softmax_scale, cu_seqlens,
+                               workspace, workspace_bytes, needed);
+  if (st != FA_OK) return st;
+  if (fa::empty_problem(pr)) return FA_OK;
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.cu_seqlens = cu_seqlens;
+  p.dsum = (float*)workspace;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.N = N;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * kLog2eF;
+  hipError_t e = fa::bwd_launch(p, d, causal, cu_seqlens != nullptr, stages, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                 const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens,
+                   workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// fa_device.h -- gfx950 device primitives shared by the attention kernels.
+//
+// MFMA operand/result layouts (checked on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//     B: lane l holds B[8 * (l / 32) + e][l % 32]
+//     D: lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+//   ds_read_b64_tr_b16 (per group of 16 lanes, each lane addressing 4 bf16):
+//     lane i receives element (i % 4) of the vectors addressed by lanes
+//     i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of its group.
+//   v_permlane32_swap(x, x) returns {x[l], x[l ^ 32]} in some order on every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Both lanes of the pair (l, l ^ 32) receive max(x[l], x[l ^ 32]).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Both lanes of the pair (l, l ^ 32) receive x[l] + x[l ^ 32].
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Two floats to packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16); `p` is this lane's 8-byte address.
+__device__ __forceinline__ bf16x4 lds_read_tr(const void FA_LDS* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 FA_LDS*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const void FA_LDS* p) {
+  return *(const bf16x8 FA_LDS*)p;
+}
+
+// One 16-byte global load per lane straight into LDS (global_load_lds_dwordx4).
+// The 64 lanes of the wave fill 1 KiB of LDS starting at `lds` (wave-uniform),
+// lane i at lds + 16 * i.
+__device__ __forceinline__ void g2lds16(const void* g, void FA_LDS* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// exp2 on the FMA pipe: exact split x = n + f with n = floor(x), f in [0, 1),
+// 2^f from a minimax polynomial (coefficients fitted by gen_exp2_poly.py),
+// 2^n applied by adding n to the exponent field. Inputs below -127 return 0
+// (so a masked -inf gives exactly 0); the result is a normal float or 0.
+#include "exp2_poly_coeffs.h"
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -127.0f);
+  float n = __builtin_floorf(x);
+  float f = x - n;
+  float p = kExp2Poly[kExp2PolyDegree];
+#pragma unroll
+  for (int i = kExp2PolyDegree - 1; i >= 0; --i) p = __builtin_fmaf(p, f, kExp2Poly[i]);
+  int e = (int)n;
+  int bits = __float_as_int(p) + (e << 23);
+  return x <= -127.0f ? 0.0f : __int_as_float(bits);
+}
+
+// XOR swizzle of the 16-byte chunks of row `row` of a bf16 [rows][D] tile in
+// LDS (physical chunk = logical chunk ^ lds_swz<D>(row)). Conflict-free for
+// both access patterns the kernels use:
+//   * 16 consecutive rows, one 16-byte chunk each (ds_read_b128 MFMA operands);
+//   * 4 consecutive rows x 4 consecutive chunks (ds_read_b64_tr_b16 groups).
+template <int D>
+__device__ __forceinline__ int lds_swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    const int x = row >> 1;   // two 128-byte rows share one 256-byte bank line
+    return ((x & 1) << 2) | ((x >> 1) & 3);
+  }
+}
+
+template <int EXPMODE>
+__device__ __forceinline__ float exp2_sel(float x) {
+  if constexpr (EXPMODE == 1) return exp2_poly(x);
+  else return __builtin_amdgcn_exp2f(x);
+}
+
+}  // namespace fa

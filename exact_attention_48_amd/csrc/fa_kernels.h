@@ -1,0 +1,48 @@
+// fa_kernels.h -- internal interface between the host dispatch and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens;   // nullptr for uniform batches
+  int B, Hq, Hkv, G, N;
+  int n_qtiles;                // query tiles per sequence (set by fwd_launch)
+  int n_items;                 // B * Hq * n_qtiles (set by fwd_launch)
+  int xcd_group;               // consecutive work items kept on one XCD (0 = off)
+  int lpt;                     // 1: heaviest query tiles first
+  float scale_log2;            // softmax_scale * log2(e)
+  float tau;                   // conditional rescale threshold (log2 units)
+};
+
+hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream);
+int fwd_block_m();
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* cu_seqlens;
+  float* dsum;                 // workspace: D_i = rowsum(dO * O), laid out like LSE
+  int B, Hq, Hkv, G, N;
+  float scale;
+  float scale_log2;
+};
+
+hipError_t bwd_launch(BwdParams p, int d, int causal, int varlen, int stages, hipStream_t stream);
+size_t bwd_workspace_bytes(long B, long Hq, long Hkv, long N, int d, int causal, int varlen);
+
+}  // namespace fa

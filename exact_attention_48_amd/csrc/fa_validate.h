@@ -1,0 +1,79 @@
+// fa_validate.h -- host-side argument checks of the C ABI (pure C++, no HIP).
+//
+// Every entry point validates all of its arguments here before anything is
+// launched, so an invalid call returns a status and enqueues nothing.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+
+namespace fa {
+
+struct Problem {
+  long B, Hq, Hkv, N, d;
+  int causal;
+  int varlen;
+};
+
+// Limits of this implementation.
+constexpr long kMaxItems = 1L << 24;        // query tiles x heads x sequences per launch
+constexpr long kMaxTokens = 1L << 31;       // tokens per tensor (B * N, or T)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Sizes, head configuration and flags shared by forward and backward.
+inline fa_status check_problem(const Problem& pr, float scale) {
+  if (pr.B < 0 || pr.N < 0 || pr.Hq <= 0 || pr.Hkv <= 0 || pr.d <= 0) return FA_ERR_INVALID_ARGUMENT;
+  if (pr.Hq % pr.Hkv != 0) return FA_ERR_INVALID_ARGUMENT;
+  if (pr.causal != 0 && pr.causal != 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return FA_ERR_INVALID_ARGUMENT;
+  if (pr.d != 64 && pr.d != 128) return FA_ERR_UNSUPPORTED;
+  if (pr.B * pr.N > kMaxTokens) return FA_ERR_UNSUPPORTED;
+  const long tiles = (pr.N + 127) / 128;
+  if (pr.B * pr.Hq * tiles > kMaxItems) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+inline bool empty_problem(const Problem& pr) { return pr.B == 0 || pr.N == 0; }
+
+inline fa_status check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const Problem& pr, float scale, const int32_t* cu_seqlens,
+                           const fa_fwd_options* opt) {
+  fa_status st = check_problem(pr, scale);
+  if (st != FA_OK) return st;
+  if (opt) {
+    if (opt->exp_mode != FA_EXP_HW && opt->exp_mode != FA_EXP_POLY) return FA_ERR_INVALID_ARGUMENT;
+    if (!(opt->rescale_tau >= 0.f && opt->rescale_tau <= 64.f)) return FA_ERR_INVALID_ARGUMENT;
+    if (opt->lpt_order != 0 && opt->lpt_order != 1) return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (empty_problem(pr)) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !aligned4(cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
+  return FA_OK;
+}
+
+inline fa_status check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, const void* dq, const void* dk, const void* dv,
+                           const Problem& pr, float scale, const int32_t* cu_seqlens,
+                           const void* workspace, size_t workspace_bytes, size_t needed) {
+  fa_status st = check_problem(pr, scale);
+  if (st != FA_OK) return st;
+  if (empty_problem(pr)) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !aligned4(cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
+  if (needed > 0) {
+    if (!workspace || workspace_bytes < needed) return FA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_INVALID_ARGUMENT;
+  }
+  return FA_OK;
+}
+
+}  // namespace fa

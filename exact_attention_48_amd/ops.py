@@ -1,0 +1,76 @@
+"""Tensor-level helpers over the C ABI: allocate outputs with PyTorch, call capi.
+
+Tensors are bf16, contiguous, on the GPU, in the layouts of include/fa.h:
+uniform Q/O [B, N, Hq, d], K/V [B, N, Hkv, d], LSE [B, Hq, N]; packed
+Q/O [T, Hq, d], K/V [T, Hkv, d], LSE [Hq, T] with int32 ``cu_seqlens``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import capi
+
+
+def _check(name: str, t: torch.Tensor, dtype=torch.bfloat16):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int]):
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("uniform batches use [B, N, H, d] tensors")
+        B, N, Hq, d = q.shape
+        if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+            raise ValueError("K/V shape does not match Q")
+        return B, N, Hq, k.shape[2], d
+    _check("cu_seqlens", cu_seqlens, torch.int32)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed batches use [T, H, d] tensors")
+    if max_seqlen is None:
+        raise ValueError("packed batches need max_seqlen (the maximum sequence length)")
+    B = cu_seqlens.numel() - 1
+    return B, int(max_seqlen), q.shape[1], k.shape[1], q.shape[2]
+
+
+def forward(q, k, v, causal: bool, scale: Optional[float] = None, cu_seqlens=None, max_seqlen=None,
+            options: Optional[capi.FaOptions] = None, stream=None, out=None, lse=None):
+    """Returns (O, LSE). ``out``/``lse`` may be preallocated."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t)
+    B, N, Hq, Hkv, d = _dims(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse_shape = (B, Hq, N) if cu_seqlens is None else (Hq, q.shape[0])
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    capi.fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens, options, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool, scale: Optional[float] = None, cu_seqlens=None,
+             max_seqlen=None, stream=None, workspace=None):
+    """Returns (dQ, dK, dV)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(n, t)
+    _check("lse", lse, torch.float32)
+    B, N, Hq, Hkv, d = _dims(q, k, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = capi.fa_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal), int(cu_seqlens is not None))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    capi.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens,
+                workspace, workspace.numel(), stream)
+    return dq, dk, dv

@@ -1,0 +1,161 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention tile by tile with an
+ * online softmax, so the N x N score matrix never reaches device memory
+ * (tiling and online softmax: "FlashAttention-4 Conquers Asymmetric GPU
+ * Hardware Scaling", podcast.app episode page, second paragraph of the
+ * description). The forward pass writes O and the per-row log-sum-exp; the
+ * backward pass recomputes the softmax and writes dQ, dK and dV (backward pass:
+ * abstract on the zhuanzhiai.com page). Causal masking and packed
+ * variable-length batches follow the daily.dev "Summary" of the Together AI
+ * post; grouped K/V heads (Hq a multiple of Hkv) are supported as well.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or synchronises. Work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream) and the call returns at
+ *    once. Device faults surface at the caller's next synchronisation.
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns; fp32 tensors hold IEEE
+ *    binary32. Every tensor is contiguous and 16-byte aligned.
+ *  - Uniform batch (cu_seqlens == NULL), "BSHD" layout:
+ *        Q, O, dO, dQ : [B, N, Hq, d]      K, V, dK, dV : [B, N, Hkv, d]
+ *        LSE          : [B, Hq, N] fp32
+ *  - Packed variable-length batch (cu_seqlens != NULL): B sequences of length
+ *    L_s = cu_seqlens[s+1] - cu_seqlens[s], packed along the token axis:
+ *        Q, O, dO, dQ : [T, Hq, d]         K, V, dK, dV : [T, Hkv, d]
+ *        LSE          : [Hq, T] fp32       T = cu_seqlens[B]
+ *    cu_seqlens is a device int32 array of B+1 entries with cu_seqlens[0] = 0,
+ *    non-decreasing, and every L_s <= N (N is the maximum length). Its contents
+ *    are not checked (that would need a synchronisation); breaking these
+ *    preconditions is undefined behaviour.
+ *  - Query head h reads K/V head h / (Hq / Hkv).
+ *  - Causal: key j is masked for query i when j > i (positions within the
+ *    sequence; queries and keys have the same length).
+ *  - Scores are S = softmax_scale * Q K^T; LSE_i = ln(sum_j exp(S_ij)).
+ *  - All arguments are validated on the host before anything is launched; an
+ *    invalid argument returns a status code and enqueues nothing.
+ *  - Supported head sizes: d = 64 and d = 128.
+ *  - Entry points are stateless and may be called concurrently from several
+ *    host threads.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, Hq % Hkv != 0, non-finite scale */
+    FA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head size other than 64 or 128) */
+    FA_ERR_WORKSPACE = 3,        /* backward workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/* Exponential used for the softmax numerators. */
+typedef enum {
+    FA_EXP_HW = 0,   /* the hardware v_exp_f32 instruction */
+    FA_EXP_POLY = 1  /* polynomial on the FMA pipe after an exact split x = n + f
+                        (software exponential with Cody-Waite range reduction:
+                        daily.dev "Summary") */
+} fa_exp_mode;
+
+/* Optional tuning knobs of the forward pass; pass NULL for the defaults. */
+typedef struct {
+    int exp_mode;        /* fa_exp_mode; default FA_EXP_HW */
+    float rescale_tau;   /* conditional rescaling threshold in log2 units: the running
+                            max, and with it O and the row sum, is only updated when it
+                            grows by more than tau ("conditional online softmax
+                            rescaling", daily.dev "Summary"). Default 8. Any tau >= 0
+                            gives the same result up to rounding. */
+    int lpt_order;       /* 1 (default): heaviest query tiles first (longest-processing-
+                            time-first, daily.dev "Summary"); 0: plain order. */
+} fa_fwd_options;
+
+/*
+ * Forward attention.
+ *   q, k, v      bf16 inputs (layouts above)
+ *   o            bf16 output, same shape as q
+ *   lse          fp32 output, per-row natural-log log-sum-exp of the scaled scores
+ *   B            batch size (uniform) or number of sequences (packed); B >= 0
+ *   Hq, Hkv      query and key/value head counts, Hq % Hkv == 0
+ *   N            sequence length (uniform) or maximum sequence length (packed); N >= 0
+ *   d            head size (64 or 128)
+ *   causal       0 or 1
+ *   softmax_scale finite scale applied to Q K^T
+ *   cu_seqlens   NULL (uniform) or device int32[B+1] (packed)
+ *   stream       hipStream_t or NULL
+ * B == 0 or N == 0 is a valid empty call and enqueues nothing.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                 const int32_t* cu_seqlens, void* stream);
+
+/* fa_fwd with explicit options (NULL = defaults). */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                    const int32_t* cu_seqlens, const fa_fwd_options* options, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (for packed batches
+ * pass the number of sequences as B and the maximum length as N; the bound
+ * B * N >= T is used). Returns 0 for empty problems.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int varlen);
+
+/*
+ * Backward attention.
+ *   q, k, v, o   bf16 forward inputs and the forward output O
+ *   lse          fp32 LSE written by fa_fwd for the same inputs
+ *   dout         bf16 upstream gradient dO, same shape as q
+ *   dq, dk, dv   bf16 outputs, shaped like q, k, v; dK/dV of a K/V head sum over its
+ *                Hq/Hkv query heads
+ *   workspace    device scratch of at least fa_bwd_workspace_size(...) bytes, 256-byte
+ *                aligned; its contents on entry do not matter and on return are undefined
+ * Other arguments as for fa_fwd. Returns FA_ERR_WORKSPACE if the workspace is
+ * NULL or too small for a non-empty problem.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                 const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of the backward pass, for fa_bwd_ex. */
+typedef enum {
+    FA_BWD_PREPROCESS = 1,  /* D_i = rowsum(dO o O) into the workspace */
+    FA_BWD_DKDV = 2,        /* dK and dV (reads D from the workspace) */
+    FA_BWD_DQ = 4,          /* dQ (reads D from the workspace) */
+    FA_BWD_ALL = 7
+} fa_bwd_stage;
+
+/*
+ * fa_bwd restricted to the stages in `stages` (a mask of fa_bwd_stage), run in
+ * the order PREPROCESS, DKDV, DQ. DKDV and DQ read what PREPROCESS wrote into the
+ * same workspace and do not depend on each other, so once PREPROCESS has run
+ * they may be enqueued separately (for instance on two streams, ordered after
+ * PREPROCESS by the caller). fa_bwd(...) is fa_bwd_ex(..., FA_BWD_ALL, stream).
+ * Returns FA_ERR_INVALID_ARGUMENT for a mask outside 1..7.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                    const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, int stages,
+                    void* stream);
+
+/* Static, human-readable description of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Library version string. */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,70 @@
+"""Shared helpers for the GPU parity tests: inputs to the device, oracle comparisons."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_48_amd import capi, inputs as I, ops
+
+# Tolerances against the float64 oracle fed the same bf16 inputs.
+O_MAX_ABS = 1e-2
+LSE_MAX_ABS = 1e-3
+GRAD_REL_FRO = 2e-2
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 tensor on cuda:0."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    """bf16 / fp32 device tensor -> float64 numpy (exact)."""
+    if t.dtype == torch.bfloat16:
+        return I.bf16_bits_to_f64(t.detach().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def f64(bits: np.ndarray) -> np.ndarray:
+    return I.bf16_bits_to_f64(bits)
+
+
+def gpu_forward(x: I.Inputs, options=None):
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    cu = torch.from_numpy(x.cu_seqlens).to("cuda:0") if x.cu_seqlens is not None else None
+    o, lse = ops.forward(q, k, v, x.causal, x.scale, cu, x.N if cu is not None else None, options)
+    torch.cuda.synchronize()
+    return q, k, v, cu, o, lse
+
+
+def oracle_forward(x: I.Inputs, rows=None):
+    return oracle.attention_forward(f64(x.q), f64(x.k), f64(x.v), x.scale, x.causal, x.cu_seqlens, rows=rows)
+
+
+def check_forward(o_gpu, lse_gpu, o_ref, lse_ref, label=""):
+    """Max-abs errors on the rows the oracle computed (others are NaN in the reference)."""
+    o = host_f64(o_gpu)
+    lse = host_f64(lse_gpu)
+    mo = ~np.isnan(o_ref)
+    ml = ~np.isnan(lse_ref)
+    assert mo.any() and ml.any()
+    assert np.all(np.isfinite(o[mo])) and np.all(np.isfinite(lse[ml])), f"{label}: non-finite output"
+    eo = float(np.max(np.abs(o[mo] - o_ref[mo])))
+    el = float(np.max(np.abs(lse[ml] - lse_ref[ml])))
+    assert eo <= O_MAX_ABS, f"{label}: O max-abs error {eo:.3e} > {O_MAX_ABS}"
+    assert el <= LSE_MAX_ABS, f"{label}: LSE max-abs error {el:.3e} > {LSE_MAX_ABS}"
+    return eo, el
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+
+
+def sampled_rows(n_first=128, n_last=128, stride=97):
+    """Row selector for long sequences: first and last rows plus a strided sample."""
+    def sel(s, L):
+        r = set(range(min(n_first, L))) | set(range(max(0, L - n_last), L)) | set(range(0, L, stride))
+        return np.array(sorted(r), dtype=np.int64)
+    return sel
