@@ -81,6 +81,17 @@ __device__ __forceinline__ void g2lds16(const void* g, void FA_LDS* lds) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt immediate: at most `vm` vector-memory operations (which include the
+// HBM->LDS copies) and no LDS operation of this wave outstanding.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
+
+// Workgroup barrier WITHOUT the memory fence of __syncthreads(): that fence
+// waits for every outstanding vector-memory operation, i.e. it would drain the
+// HBM->LDS copies still in flight for later tiles. Callers wait explicitly for
+// the copies they need (s_waitcnt) before calling this; the memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
 // exp2 on the FMA pipe: exact split x = n + f with n = floor(x), f in [0, 1),
 // 2^f from a minimax polynomial (coefficients fitted by gen_exp2_poly.py),
 // 2^n applied by adding n to the exponent field. Inputs below -127 return 0
