@@ -251,18 +251,33 @@ def main():
             cores = int(blas[0]["num_threads"]) if blas else os.cpu_count()
         except Exception:
             cores = os.cpu_count()
-        n_heads = args.cpu_heads or 16
+        # Heads of the same workload, one (batch, head) pair at a time, until
+        # about 12 s of oracle work (or --cpu-heads pairs, or all of them).
         f64 = I.bf16_bits_to_f64
-        qh, kh, vh, doh = (f64(t[0:1, :, :n_heads]) for t in (x.q, x.k, x.v, x.do))
-        c0 = time.perf_counter()
-        oracle.attention_forward(qh, kh, vh, scale, bool(causal))
-        oracle.attention_backward(qh, kh, vh, doh, scale, bool(causal))
-        secs = time.perf_counter() - c0
-        fl = I.counted_flops([N], n_heads, d, bool(causal)) + I.counted_flops([N], n_heads, d, bool(causal), True)
+        pairs = [(b, hh) for b in range(B) for hh in range(Hq)]
+        budget = 12.0
+        secs, done = 0.0, 0
+        for (b, hh) in pairs:
+            if args.cpu_heads and done >= args.cpu_heads:
+                break
+            if not args.cpu_heads and secs >= budget:
+                break
+            g = hh // (Hq // Hkv)
+            qh = f64(x.q[b:b + 1, :, hh:hh + 1])
+            kh, vh = f64(x.k[b:b + 1, :, g:g + 1]), f64(x.v[b:b + 1, :, g:g + 1])
+            doh = f64(x.do[b:b + 1, :, hh:hh + 1])
+            c0 = time.perf_counter()
+            oracle.attention_forward(qh, kh, vh, scale, bool(causal))
+            oracle.attention_backward(qh, kh, vh, doh, scale, bool(causal))
+            secs += time.perf_counter() - c0
+            done += 1
+        fl = (I.counted_flops([N], done, d, bool(causal)) +
+              I.counted_flops([N], done, d, bool(causal), backward=True))
         cpu = {"value": round(fl / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                "seconds": round(secs, 2),
-               "sample": f"float64 NumPy oracle, forward + backward of {n_heads} of the {B * Hq} (batch, head) "
-                         f"pairs of the same workload (N={N}, d={d}), counted FLOP / wall time"}
+               "sample": f"float64 NumPy oracle, forward + backward of {done} of the {B * Hq} (batch, head) "
+                         f"pairs of the same workload (N={N}, d={d}), one pair per call, counted FLOP / oracle "
+                         f"wall time"}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -94,19 +94,19 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 
 // exp2 on the FMA pipe: exact split x = n + f with n = floor(x), f in [0, 1),
 // 2^f from a minimax polynomial (coefficients fitted by gen_exp2_poly.py),
-// 2^n applied by adding n to the exponent field. Inputs below -127 return 0
-// (so a masked -inf gives exactly 0); the result is a normal float or 0.
+// 2^n applied by adding n to the exponent field. Inputs below -125 return 0
+// (so a masked -inf gives exactly 0 and no result is denormal: p(f) may be
+// slightly below 1, which would push 2^-126 p(f) out of the normal range).
 #include "exp2_poly_coeffs.h"
 __device__ __forceinline__ float exp2_poly(float x) {
-  x = fmaxf(x, -127.0f);
-  float n = __builtin_floorf(x);
-  float f = x - n;
+  const float xc = fmaxf(x, -125.0f);
+  const float n = __builtin_floorf(xc);
+  const float f = xc - n;
   float p = kExp2Poly[kExp2PolyDegree];
 #pragma unroll
   for (int i = kExp2PolyDegree - 1; i >= 0; --i) p = __builtin_fmaf(p, f, kExp2Poly[i]);
-  int e = (int)n;
-  int bits = __float_as_int(p) + (e << 23);
-  return x <= -127.0f ? 0.0f : __int_as_float(bits);
+  const int bits = __float_as_int(p) + ((int)n << 23);
+  return x < -125.0f ? 0.0f : __int_as_float(bits);
 }
 
 // XOR swizzle of the 16-byte chunks of row `row` of a bf16 [rows][D] tile in

@@ -1,0 +1,111 @@
+"""The C ABI loads, exports what include/fa.h declares, and validates on the host (CPU only).
+
+Every call here is rejected by the host-side checks (or is an empty problem),
+so nothing is launched and no GPU is needed.
+"""
+import math
+import os
+import re
+
+import pytest
+
+from exact_attention_48_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x100000   # a 16-byte aligned fake device address (never dereferenced: validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(capi.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return capi.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(capi.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings(lib):
+    for st in (capi.FA_OK, capi.FA_ERR_INVALID_ARGUMENT, capi.FA_ERR_UNSUPPORTED, capi.FA_ERR_WORKSPACE,
+               capi.FA_ERR_HIP):
+        assert capi.fa_status_string(st).startswith("FA_")
+    assert "unknown" in capi.fa_status_string(99)
+    assert "gfx950" in capi.fa_version()
+
+
+def fwd(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, scale=0.1, cu=None, opt=None):
+    return capi.fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, cu, opt, stream=0, check=False)
+
+
+# Every case is invalid, so validation returns before any HIP call.
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(lse=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), capi.FA_ERR_UNSUPPORTED),
+    (dict(d=256), capi.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hkv=0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-5), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=A + 8), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(lse=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(cu=A + 1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=1 << 20, N=1 << 20), capi.FA_ERR_UNSUPPORTED),
+    (dict(opt=capi.FaOptions(7, 8.0, 1)), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(0, -1.0, 1)), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(0, 8.0, 2)), capi.FA_ERR_INVALID_ARGUMENT),
+])
+def test_forward_rejects(lib, kw, expect):
+    assert fwd(**kw) == expect
+
+
+def test_empty_forward_is_ok_without_pointers(lib):
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, B=0) == capi.FA_OK
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, N=0) == capi.FA_OK
+
+
+def bwd(*, ws=A, ws_bytes=1 << 30, stages=capi.FA_BWD_ALL, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0,
+                scale=0.1, cu=None)
+    args.update(kw)
+    return capi.fa_bwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
+                          args["dk"], args["dv"], args["B"], args["Hq"], args["Hkv"], args["N"], args["d"],
+                          args["causal"], args["scale"], args["cu"], ws, ws_bytes, stages, stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ws=None, ws_bytes=0), capi.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1), capi.FA_ERR_WORKSPACE),
+    (dict(ws=A + 16), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(dq=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(dv=A + 4), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=32), capi.FA_ERR_UNSUPPORTED),
+    (dict(Hq=4, Hkv=3), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(stages=0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(stages=8), capi.FA_ERR_INVALID_ARGUMENT),
+])
+def test_backward_rejects(lib, kw, expect):
+    assert bwd(**kw) == expect
+
+
+def test_workspace_size(lib):
+    assert capi.fa_bwd_workspace_size(0, 2, 2, 128, 128, 1, 0) == 0
+    assert capi.fa_bwd_workspace_size(2, 16, 16, 8192, 128, 1, 0) == 2 * 8192 * 16 * 4
+    n = capi.fa_bwd_workspace_size(3, 5, 5, 7, 64, 0, 1)
+    assert n >= 3 * 7 * 5 * 4 and n % 256 == 0
