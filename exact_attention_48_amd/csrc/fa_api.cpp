@@ -25,7 +25,8 @@ size_t bwd_workspace_bytes(long B, long Hq, long Hkv, long N, int d, int causal,
   if (B <= 0 || N <= 0 || Hq <= 0) return 0;
   (void)d;
   const size_t rows = (size_t)B * (size_t)N;          // >= T for packed batches
-  return round256(rows * (size_t)Hq * sizeof(float)); // D_i, laid out like the LSE
+  // D_i and LSE_i * log2(e), each laid out like the LSE
+  return 2 * round256(rows * (size_t)Hq * sizeof(float));
 }
 
 }  // namespace fa
@@ -107,6 +108,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   p.dv = dv;
   p.cu_seqlens = cu_seqlens;
   p.dsum = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + needed / 2);
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -8,18 +8,36 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, all on the caller's stream:
-//   1. bwd_dsum_kernel: D_i = rowsum(dO o O) in fp32 (HBM-bound, one pass).
-//   2. bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128-key tile);
-//      each wave keeps 32 keys' K and V fragments in registers and streams the
-//      64-row Q / dO tiles of every query head of the group through LDS, so the
-//      group's dK/dV sum needs no atomics. Per tile and wave: S = Q K^T and
-//      dP = dO V^T with the key in the lane (C layout), dV^T += dO^T P and
-//      dK^T += Q^T dS with the transposed Q / dO operands read by
-//      ds_read_b64_tr_b16.
+//   1. bwd_prep_kernel: D_i = rowsum(dO o O) and LSE_i * log2(e), fp32, into
+//      the workspace (HBM-bound, one pass).
+//   2. bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128-key tile),
+//      one wave per SIMD. Each wave keeps 32 keys' K and V fragments and their
+//      dK/dV accumulators in registers and streams the 64-row Q / dO tiles of
+//      every query head of the group, so the group's dK/dV sum needs no
+//      atomics. Per tile and wave: S = Q K^T and dP = dO V^T with the key in
+//      the lane (C layout), P and dS in bf16, dV^T += dO^T P and dK^T += Q^T dS
+//      with the transposed Q / dO operands read by ds_read_b64_tr_b16.
 //   3. bwd_dq_kernel: one workgroup per (sequence, query head, 128-query tile),
-//      mirroring the forward: S^T = K Q^T and dP^T = V dO^T with the query in
-//      the lane, then dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16).
-// dQ is produced by this separate pass rather than by atomic adds from kernel 2.
+//      one wave per SIMD: S^T = K Q^T and dP^T = V dO^T with the query in the
+//      lane, then dQ^T += K^T dS^T (K^T through ds_read_b64_tr_b16).
+// dQ is produced by this separate pass rather than by fp32 atomic adds from
+// kernel 2: on this GPU those run at about one 4-byte add per L2 channel and
+// clock, which for long sequences costs more than recomputing S and dP.
+//
+// Both main kernels are software-pipelined the same way. Tiles stream
+// HBM -> LDS (global_load_lds_dwordx4, no register staging) through a ring of
+// NSTAGE = 4 distinct LDS objects, issued two iterations ahead; one workgroup
+// barrier per iteration (without the memory fence of __syncthreads, which
+// would drain the copies in flight). Iteration i of a wave runs
+//   phase A: the MFMAs of S, dP for tile i+1, slot by slot interleaved with the
+//            softmax VALU work of tile i (its S, dP came from phase A of the
+//            previous iteration), so the matrix core and the VALU overlap;
+//   phase B: the MFMAs that consume tile i's P and dS (dV, dK or dQ), their
+//            transposed operands read a few MFMAs ahead.
+// Masking code runs only for tiles that cross the causal diagonal or the end
+// of a sequence.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -29,37 +47,92 @@ namespace {
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
+constexpr int NSTAGE = 4;     // LDS ring depth
+constexpr int TROWS = 64;     // rows per streamed tile (Q/dO or K/V)
 constexpr int KV_BN = 128;    // keys per dK/dV workgroup (32 per wave)
-constexpr int KV_BM = 64;     // query rows per streamed tile in the dK/dV kernel
 constexpr int Q_BM = 128;     // queries per dQ workgroup (32 per wave)
-constexpr int Q_BN = 64;      // keys per streamed tile in the dQ kernel
+constexpr int PF = 4;         // MFMA operands read ahead
 
-// Copy `nrows` rows (clamped to L-1) of a [tokens][row_stride] bf16 tensor into a
-// swizzled LDS tile [nrows][D]; all NTHREADS threads take part.
-template <int D, int NROWS>
-__device__ __forceinline__ void load_rows(char FA_LDS* dst, const char* gbase, long row_stride_b, int r0, int L,
-                                          int wave, int lane) {
-  constexpr int ROWB = D * 2;
-  constexpr int LPR = ROWB / 16;
-  constexpr int RPI = 64 / LPR;
-  constexpr int NI = NROWS / RPI;
-  static_assert(NI % NWAVES == 0, "tile rows must split evenly over the waves");
-  constexpr int PER_WAVE = NI / NWAVES;
-  const int r_in = lane / LPR;
-  const int pos = lane % LPR;
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    const int ins = wave * PER_WAVE + u;
-    const int row = ins * RPI + r_in;
-    int g = r0 + row;
-    g = g < L ? g : L - 1;
-    g2lds16(gbase + (long)g * row_stride_b + (pos ^ lds_swz<D>(row)) * 16, dst + ins * 1024);
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// HBM -> LDS copy of a TROWS x D bf16 tile of a [tokens][stride] tensor into a
+// swizzled LDS tile; rows past the sequence end are clamped to its last row.
+// All NWAVES waves take part, PER_WAVE 1 KiB instructions each.
+template <int D>
+struct RowCopy {
+  static constexpr int ROWB = D * 2;
+  static constexpr int LPR = ROWB / 16;          // lanes per row
+  static constexpr int RPI = 64 / LPR;           // rows per instruction
+  static constexpr int NI = TROWS / RPI;         // instructions per tile
+  static constexpr int PER_WAVE = NI / NWAVES;
+  static_assert(PER_WAVE * NWAVES == NI, "tile copy must split evenly over the waves");
+  unsigned off[PER_WAVE];                        // row * stride + swizzled chunk * 16
+  int wave, lane;
+
+  __device__ __forceinline__ int row(int u) const { return (wave * PER_WAVE + u) * RPI + lane / LPR; }
+  __device__ __forceinline__ unsigned chunk16(int u) const {
+    return (unsigned)(((lane % LPR) ^ lds_swz<D>(row(u))) * 16);
   }
-}
+  __device__ __forceinline__ void init(int wave_, int lane_, unsigned stride) {
+    wave = wave_;
+    lane = lane_;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) off[u] = (unsigned)row(u) * stride + chunk16(u);
+  }
+  // `base` points at token 0 of this head; rows r0 .. r0 + TROWS - 1.
+  __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int r0, int L) const {
+    const char* tb = base + (long)r0 * stride;
+    char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
+    if (r0 + TROWS <= L) {
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        unsigned o = off[u];
+        asm volatile("" : "+v"(o));   // keep the 64-bit address out of loop-invariant code motion
+        g2lds16(tb + o, dst + u * 1024);
+      }
+    } else {
+      const int last = L - 1 - r0;
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const int r = min(row(u), last);
+        g2lds16(tb + ((unsigned)r * (unsigned)stride + chunk16(u)), dst + u * 1024);
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ long lse_index(const BwdParams& p, int s, int h, int seq0, int row, int T, bool varlen) {
   return varlen ? (long)h * T + seq0 + row : ((long)s * p.Hq + h) * p.N + row;
 }
+
+// Per-lane LDS offsets of the MFMA operands in a swizzled [64][D] bf16 tile.
+// The swizzle only XORs chunk bits, so other k-steps / d-blocks are an XOR away:
+//   row operand (ds_read_b128) of k-step ks, rows 32 qb + l32:  (aoff ^ (ks << 5)) + qb * 32 * ROWB
+//   transposed operand (two ds_read_b64_tr_b16) of d-block db, rows 16 t + ...:
+//                         (troff[i] ^ (db << 6)) + t * 16 * ROWB, i = 0, 1
+template <int D>
+struct TileOffsets {
+  int aoff;
+  int troff[2];
+  __device__ __forceinline__ void init(int lane) {
+    constexpr int ROWB = D * 2;
+    const int hl = lane >> 5, l32 = lane & 31, g16 = lane & 15;
+    aoff = l32 * ROWB + ((hl ^ lds_swz<D>(l32)) << 4);
+    const int dcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+    const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
+    const int r0 = 4 * hl + (g16 >> 2), r1 = r0 + 8;
+    troff[0] = r0 * ROWB + ((chunk ^ lds_swz<D>(r0)) * 16) + sub;
+    troff[1] = r1 * ROWB + ((chunk ^ lds_swz<D>(r1)) * 16) + sub;
+  }
+  __device__ __forceinline__ bf16x8 row_operand(const char FA_LDS* tile, int ks, int blk) const {
+    return lds_read16(tile + (aoff ^ (ks << 5)) + blk * 32 * D * 2);
+  }
+  __device__ __forceinline__ bf16x8 tr_operand(const char FA_LDS* tile, int t, int db) const {
+    return cat(lds_read_tr(tile + (troff[0] ^ (db << 6)) + t * 16 * D * 2),
+               lds_read_tr(tile + (troff[1] ^ (db << 6)) + t * 16 * D * 2));
+  }
+};
 
 // Stage a wave's 32 x D fp32 accumulator (transposed C layout: lane = row
 // l32, register r of block db = column db*32 + 8(r/4) + 4(l/32) + r%4) as bf16
@@ -91,13 +164,29 @@ __device__ __forceinline__ void store_rows_bf16(char FA_LDS* st, const f32x16* a
   }
 }
 
+// Wait until at most `n` vector-memory operations of this wave are outstanding
+// (and no LDS operation); n is one of the few values the kernels use.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(10)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(16)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(18)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_k dO[i,k] O[i,k]
+// 1. D_i = sum_k dO[i,k] O[i,k]  and  LSE_i * log2(e)
 // ---------------------------------------------------------------------------
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256) void bwd_dsum_kernel(const BwdParams p, long total_rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, long total_rows) {
   constexpr int LPR = D / 8;                 // lanes per (token, head) row, 16 B each
   constexpr int RPB = 256 / LPR;             // rows per block
   const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -124,6 +213,7 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(const BwdParams p, long t
       idx = (b * p.Hq + h) * p.N + n;
     }
     p.dsum[idx] = acc;
+    p.lse2[idx] = p.lse[idx] * kLog2e;
   }
 }
 
@@ -131,39 +221,43 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(const BwdParams p, long t
 // 2. dK, dV: KV-major
 // ---------------------------------------------------------------------------
 template <int D>
-struct KvSmem {
+struct KvStage {
   static constexpr int ROWB = D * 2;
-  static constexpr int TILEB = KV_BM * ROWB;          // one Q or dO tile
-  static constexpr int STAGEB = 2 * TILEB + 2 * KV_BM * 4;   // Q, dO, LSE, D
-  static constexpr int OROWB = ROWB + 16;
-  static_assert(2 * 32 * OROWB <= STAGEB, "two waves' output staging must fit in one stage");
+  static constexpr int TILEB = TROWS * ROWB;          // one Q or dO tile
+  static constexpr int LSEOFF = 2 * TILEB;            // 64 x LSE*log2(e), then 64 x D
+  static constexpr int BYTES = 2 * TILEB + 2 * TROWS * 4;
+  static constexpr int OROWB = ROWB + 16;             // output staging pitch
+  static_assert(32 * OROWB <= BYTES, "a wave's output staging must fit in one stage");
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const BwdParams p) {
-  using S = KvSmem<D>;
+  using S = KvStage<D>;
+  using RC = RowCopy<D>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  // two distinct LDS objects so reads of one stage never wait on the copy into the other
-  __shared__ __attribute__((aligned(1024))) char stage0_raw[S::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char stage1_raw[S::STAGEB];
-  char FA_LDS* stage0 = (char FA_LDS*)stage0_raw;
-  char FA_LDS* stage1 = (char FA_LDS*)stage1_raw;
+  constexpr int ROWB = S::ROWB;
+  constexpr int OPS = 1 + 2 * RC::PER_WAVE;          // copy instructions per tile and wave
+  __shared__ __attribute__((aligned(1024))) char s0_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s1_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s2_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s3_raw[S::BYTES];
+  char FA_LDS* const stg[NSTAGE] = {(char FA_LDS*)s0_raw, (char FA_LDS*)s1_raw, (char FA_LDS*)s2_raw,
+                                    (char FA_LDS*)s3_raw};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
   // work item: level-major (key tile 0 first: under causal masking it sees the
   // most query tiles), then (sequence, K/V head)
-  const int n_kt = (p.N + KV_BN - 1) / KV_BN;
   const int per_level = p.B * p.Hkv;
   const int w = blockIdx.x;
   const int kt = w / per_level;
   const int rr = w - kt * per_level;
   const int s = rr / p.Hkv;
   const int hkv = rr - s * p.Hkv;
-  (void)n_kt;
 
   int seq0, L, T = 0;
   if constexpr (VARLEN) {
@@ -180,8 +274,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int my_key = kw0 + l32;
 
   const long kv_stride = (long)p.Hkv * D;    // elements per token
-  const long q_stride = (long)p.Hq * D;
-  // K, V fragments of this lane's key (B operands): [d = 16 ks + 8 hl + e]
+  const long q_stride_b = (long)p.Hq * D * 2;
+  const int qt0 = CAUSAL ? kv0 / TROWS : 0;  // first query tile any key of the workgroup sees
+  const int n_qt = (L + TROWS - 1) / TROWS;
+  const int n_it = (n_qt - qt0) * p.G;       // (query head, query tile) pairs, head-major
+
+  // ---- K, V fragments of this lane's key (B operands): [d = 16 ks + 8 hl + e] ----
   bf16x8 kf[KSTEPS], vf[KSTEPS];
   {
     const int kr = my_key < L ? my_key : L - 1;
@@ -193,127 +291,208 @@ void bwd_dkdv_kernel(const BwdParams p) {
       vf[ks] = *(const bf16x8*)(vp + ks * 16);
     }
   }
+
+  // ---- tile copies: tile `it` = (head gi, query tile qt), issued in order ----
+  RC copy;
+  copy.init(wave, lane, (unsigned)q_stride_b);
+  int iss_g = 0, iss_qt = qt0;
+  auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
+    const int h = hkv * p.G + iss_g;
+    const int q0 = iss_qt * TROWS;
+    // LSE*log2(e) and D of the tile's rows: wave w moves rows (w & 1) * 32 + lane
+    // of array w >> 1 (lanes 0..31)
+    if (lane < 32) {
+      int r = q0 + (wave & 1) * 32 + lane;
+      r = r < L ? r : L - 1;
+      const long li = lse_index(p, s, h, seq0, r, T, VARLEN);
+      const float* src = (wave < 2 ? p.lse2 : p.dsum) + li;
+      __builtin_amdgcn_global_load_lds(src, stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128, 4, 0,
+                                       0);
+    }
+    const char* qb = (const char*)p.q + ((long)seq0 * p.Hq + h) * D * 2;
+    const char* ob = (const char*)p.dout + ((long)seq0 * p.Hq + h) * D * 2;
+    copy.issue(stage, qb, q_stride_b, q0, L);
+    copy.issue(stage + S::TILEB, ob, q_stride_b, q0, L);
+    if (++iss_qt == n_qt) {
+      iss_qt = qt0;
+      ++iss_g;
+    }
+  };
+  issue_next(stg[0]);
+  if (n_it > 1) issue_next(stg[1]);
+  if (n_it > 2) issue_next(stg[2]);
+
+  TileOffsets<D> to;
+  to.init(lane);
+  const int lse_lane = 16 * hl;                  // byte offset of rows 4 hl .. 4 hl + 3 in a group of 8
   f32x16 dk[DBLK], dv[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) {
     dk[i] = f32x16{};
     dv[i] = f32x16{};
   }
-
-  const int qt0 = CAUSAL ? kv0 / KV_BM : 0;
-  const int n_qt = (L + KV_BM - 1) / KV_BM;
-  const int per_head = n_qt - qt0;
-  const int n_it = per_head * p.G;
+  f32x16 sA[2], pA[2], sB[2], pB[2];             // S, dP of two consecutive tiles (by tile parity)
+  u32x4 pb[4], dsb[4];                           // P, dS (bf16 pairs) of the current tile
   const float c = p.scale_log2;
 
-  auto issue = [&](int it, char FA_LDS* stage) {
-    const int gi = it / per_head;
-    const int qt = qt0 + (it - gi * per_head);
-    const int h = hkv * p.G + gi;
-    const int q0 = qt * KV_BM;
-    const char* qb = (const char*)p.q + ((long)seq0 * p.Hq + h) * D * 2;
-    const char* ob = (const char*)p.dout + ((long)seq0 * p.Hq + h) * D * 2;
-    load_rows<D, KV_BM>(stage, qb, q_stride * 2, q0, L, wave, lane);
-    load_rows<D, KV_BM>(stage + S::TILEB, ob, q_stride * 2, q0, L, wave, lane);
-    if (wave == 0) {
-      int r = q0 + lane;
-      r = r < L ? r : L - 1;
-      const long li = lse_index(p, s, h, seq0, r, T, VARLEN);
-      __builtin_amdgcn_global_load_lds(p.lse + li, stage + 2 * S::TILEB, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(p.dsum + li, stage + 2 * S::TILEB + KV_BM * 4, 4, 0, 0);
+  // S, dP of one tile (phase-A MFMAs): slot j = (k-step j / 4, operand j % 4:
+  // S block 0, S block 1, dP block 0, dP block 1).
+  constexpr int NA = 4 * KSTEPS;
+  auto a_fetch = [&](const char FA_LDS* tile, int j) __attribute__((always_inline)) {
+    const int ks = j >> 2, cc = j & 3;
+    return to.row_operand(tile + (cc >> 1) * S::TILEB, ks, cc & 1);
+  };
+  auto a_step = [&](f32x16 (&sx)[2], f32x16 (&px)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
+    const int ks = j >> 2, cc = j & 3;
+    f32x16& acc = cc < 2 ? sx[cc & 1] : px[cc & 1];
+    const bf16x8& b = cc < 2 ? kf[ks] : vf[ks];
+    if (ks == 0) mfma_v_first(acc, a, b);
+    else mfma_v(acc, a, b);
+  };
+
+  // Phase A without softmax work (first tile).
+  auto phase_a0 = [&](const char FA_LDS* tile, f32x16 (&sx)[2], f32x16 (&px)[2]) __attribute__((always_inline)) {
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(tile, i);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const bf16x8 a = qa[j % PF];
+      if (j + PF < NA) qa[j % PF] = a_fetch(tile, j + PF);
+      a_step(sx, px, j, a);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  issue(0, stage0);
-  wait_vmem();
-  __syncthreads();
-
-  const int g16 = lane & 15;
-  auto step = [&](char FA_LDS* cur, char FA_LDS* nxt, const int it) __attribute__((always_inline)) {
-    if (it + 1 < n_it) issue(it + 1, nxt);
-    const int qt = qt0 + (it % per_head);
-    const int q0 = qt * KV_BM;
-    // causal: this wave's keys see queries >= kw0 only
-    const bool active = !CAUSAL || (q0 + KV_BM - 1 >= kw0);
-    if (active) {
-      const char FA_LDS* qtile = cur;
-      const char FA_LDS* otile = cur + S::TILEB;
-      const float FA_LDS* lse_s = (const float FA_LDS*)(cur + 2 * S::TILEB);
-      const float FA_LDS* dsum_s = lse_s + KV_BM;
-      // S = Q K^T and dP = dO V^T for 2 x 32 query rows; lane = key
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      f32x16 pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int row = qb * 32 + l32;
-          const int off = row * S::ROWB + (((2 * ks + hl) ^ lds_swz<D>(row)) * 16);
-          sacc[qb] = mfma32(lds_read16(qtile + off), kf[ks], sacc[qb]);
-          pacc[qb] = mfma32(lds_read16(otile + off), vf[ks], pacc[qb]);
-        }
+  // Phase A: S, dP of the next tile (`nt`, into sx/px) interleaved with the
+  // softmax of the current tile (`ct`, rows q0.., S/dP in sc/pc) -> pb, dsb.
+  // Element e of the current tile: block qb = e / 16, register r = e % 16,
+  // query row qb*32 + 8(r/4) + 4 hl + r%4, key = this lane's key.
+  auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2],
+                     f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int q0)
+                     __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int EPS = 32 / NA;                 // softmax elements per MFMA slot
+    const float FA_LDS* lz = (const float FA_LDS*)(ct + S::LSEOFF + lse_lane);
+    const float FA_LDS* dz = lz + TROWS;
+    f32x4 lg[8], dg[8];                          // LSE2 / D of the 8 row groups (qb, r/4)
+    auto g_fetch = [&](int k) __attribute__((always_inline)) {
+      lg[k] = *(const f32x4 FA_LDS*)(lz + (k >> 2) * 32 + (k & 3) * 8);
+      dg[k] = *(const f32x4 FA_LDS*)(dz + (k >> 2) * 32 + (k & 3) * 8);
+    };
+    float pv[2], dv2[2];
+    auto elem = [&](int e) __attribute__((always_inline)) {
+      const int qb = e >> 4, r = e & 15, k = e >> 2, u = e & 3;
+      if (u == 0 && k + 1 < 8) g_fetch(k + 1);
+      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][r], c, -lg[k][u]));
+      if constexpr (MASK) {
+        const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool dead = (q >= L) || (CAUSAL && my_key > q);
+        pe = dead ? 0.f : pe;
       }
-      // P = exp2(S c - LSE log2e); dS = P (dP - D)
-      const bool need_mask = (CAUSAL && (kw0 + 31 > q0)) || (q0 + KV_BM > L) || (kw0 + 32 > L);
-      bf16x8 pb[4], db8[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qr = qb * 32 + 8 * g + 4 * hl;     // first of 4 query rows
-          const f32x4 lz = *(const f32x4 FA_LDS*)(lse_s + qr);
-          const f32x4 dz = *(const f32x4 FA_LDS*)(dsum_s + qr);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * g + u;
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -lz[u] * kLog2e));
-            if (need_mask) {
-              const int q = q0 + qr + u;
-              const bool dead = (q >= L) || (my_key >= L) || (CAUSAL && my_key > q);
-              pe = dead ? 0.f : pe;
-            }
-            pv[u] = pe;
-            dsv[u] = pe * (pacc[qb][r] - dz[u]);
-          }
-          const int t = qb * 2 + (g >> 1), e0 = (g & 1) * 4;
-          const bf16x2 p01 = pack_bf16(pv[0], pv[1]), p23 = pack_bf16(pv[2], pv[3]);
-          const bf16x2 d01 = pack_bf16(dsv[0], dsv[1]), d23 = pack_bf16(dsv[2], dsv[3]);
-          pb[t][e0 + 0] = p01[0];
-          pb[t][e0 + 1] = p01[1];
-          pb[t][e0 + 2] = p23[0];
-          pb[t][e0 + 3] = p23[1];
-          db8[t][e0 + 0] = d01[0];
-          db8[t][e0 + 1] = d01[1];
-          db8[t][e0 + 2] = d23[0];
-          db8[t][e0 + 3] = d23[1];
-        }
+      pv[e & 1] = pe;
+      dv2[e & 1] = pe * (pc[qb][r] - dg[k][u]);
+      if (e & 1) {
+        // pair (e-1, e) -> positions of the B operand of key step t = qb*2 + (r/8)
+        const int t = qb * 2 + (r >> 3), pos = (r & 7) >> 1;
+        pb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(pv[0], pv[1]));
+        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (A operands through transposing reads)
+    };
+    g_fetch(0);
+    bf16x8 qa[PF];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r0 = 16 * t + 4 * hl + (g16 >> 2), r1 = r0 + 8;
+    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(nt, i);
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int dcol = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
-          const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
-          const int o0 = r0 * S::ROWB + ((chunk ^ lds_swz<D>(r0)) * 16) + sub;
-          const int o1 = r1 * S::ROWB + ((chunk ^ lds_swz<D>(r1)) * 16) + sub;
-          dv[db] = mfma32(cat(lds_read_tr(otile + o0), lds_read_tr(otile + o1)), pb[t], dv[db]);
-          dk[db] = mfma32(cat(lds_read_tr(qtile + o0), lds_read_tr(qtile + o1)), db8[t], dk[db]);
-        }
-      }
+    for (int j = 0; j < NA; ++j) {
+      const bf16x8 a = qa[j % PF];
+      if (j + PF < NA) qa[j % PF] = a_fetch(nt, j + PF);
+      a_step(sx, px, j, a);
+#pragma unroll
+      for (int x = 0; x < EPS; ++x) elem(j * EPS + x);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmem();
-    __syncthreads();
   };
-  for (int it = 0; it < n_it; it += 2) {
-    step(stage0, stage1, it);
-    if (it + 1 < n_it) step(stage1, stage0, it + 1);
+
+  // Phase B: dV^T += dO^T P, dK^T += Q^T dS for the current tile. Step i:
+  // key step t = i / (2 DBLK), d-block db = (i / 2) % DBLK, dV (even i) or dK.
+  constexpr int NB = 8 * DBLK;
+  auto phase_b = [&](const char FA_LDS* ct) __attribute__((always_inline)) {
+    auto fetch = [&](int i) __attribute__((always_inline)) {
+      const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
+      return to.tr_operand(ct + ((i & 1) ? 0 : S::TILEB), t, db);
+    };
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = fetch(i);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 2");   // VALU-written B operands -> first MFMA
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const bf16x8 a = qa[i % PF];
+      if (i + PF < NB) qa[i % PF] = fetch(i + PF);
+      const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
+      if (i & 1) mfma_a(dk[db], a, __builtin_bit_cast(bf16x8, dsb[t]));
+      else mfma_a(dv[db], a, __builtin_bit_cast(bf16x8, pb[t]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: K/V fragments and tile 0 in, S/dP of tile 0 ----
+  if (n_it > 2) wait_vm(2 * OPS);
+  else if (n_it > 1) wait_vm(OPS);
+  else wait_vm(0);
+  barrier_no_fence();
+  phase_a0(stg[0], sA, pA);
+  mfma_result_wait();
+
+  int cur_qt = qt0;
+  // Iteration i (BI = i % NSTAGE): tile i in stg[BI], tile i+1 in stg[BI+1],
+  // tile i+3 is copied into stg[BI+3] (last read as tile i-1, before this
+  // iteration's barrier).
+  auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
+    constexpr int BI = decltype(bi_tag)::value;
+    if (i + 2 < n_it) wait_vm(OPS);
+    else if (i + 1 < n_it) wait_vm(0);
+    barrier_no_fence();
+    if (i + 3 < n_it) issue_next(stg[(BI + 3) % NSTAGE]);
+    const int q0 = cur_qt * TROWS;
+    if (++cur_qt == n_qt) cur_qt = qt0;
+    const bool need_mask = (q0 + TROWS > L) || (CAUSAL && kw0 + 31 > q0);
+    // the S/dP MFMAs of tile i+1 also run on the last iteration (on stale LDS,
+    // results unused) so that the code has a single shape
+    if constexpr (BI % 2 == 0) {
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0);
+    } else {
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0);
+    }
+    phase_b(stg[BI]);
+  };
+  for (int i = 0; i < n_it; i += NSTAGE) {
+    iter(ic<0>{}, i);
+    if (i + 1 < n_it) iter(ic<1>{}, i + 1);
+    if (i + 2 < n_it) iter(ic<2>{}, i + 2);
+    if (i + 3 < n_it) iter(ic<3>{}, i + 3);
   }
+  // the last tile's S/dP MFMAs (results unused) and the dK/dV MFMAs must be
+  // done before their registers are reused or read
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    keep_live(sA[x]);
+    keep_live(pA[x]);
+    keep_live(sB[x]);
+    keep_live(pB[x]);
+  }
+  mfma_result_wait();
 
-  // epilogue: dK = scale dK^T, dV = dV^T, staged as bf16 rows
-  char FA_LDS* st = (wave < 2 ? stage0 : stage1) + (wave & 1) * 32 * S::OROWB;
+  // ---- epilogue: dK = scale dK^T, dV = dV^T, staged as bf16 rows ----
+  barrier_no_fence();
+  char FA_LDS* st = stg[0];
+  if (wave == 1) st = stg[1];
+  if (wave == 2) st = stg[2];
+  if (wave == 3) st = stg[3];
   __bf16* dkb = (__bf16*)p.dk + ((long)seq0 * p.Hkv + hkv) * D;
   __bf16* dvb = (__bf16*)p.dv + ((long)seq0 * p.Hkv + hkv) * D;
   store_rows_bf16<D>(st, dk, p.scale, dkb, kv_stride, kw0, L, lane);
@@ -326,26 +505,31 @@ void bwd_dkdv_kernel(const BwdParams p) {
 // 3. dQ: Q-major
 // ---------------------------------------------------------------------------
 template <int D>
-struct QSmem {
+struct QStage {
   static constexpr int ROWB = D * 2;
-  static constexpr int TILEB = Q_BN * ROWB;
-  static constexpr int STAGEB = 2 * TILEB;           // K, V
+  static constexpr int TILEB = TROWS * ROWB;          // one K or V tile
+  static constexpr int BYTES = 2 * TILEB;
   static constexpr int OROWB = ROWB + 16;
-  static_assert(2 * 32 * OROWB <= STAGEB, "two waves' output staging must fit in one stage");
+  static_assert(32 * OROWB <= BYTES, "a wave's output staging must fit in one stage");
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
-  using S = QSmem<D>;
+  using S = QStage<D>;
+  using RC = RowCopy<D>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  __shared__ __attribute__((aligned(1024))) char stage0_raw[S::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char stage1_raw[S::STAGEB];
-  char FA_LDS* stage0 = (char FA_LDS*)stage0_raw;
-  char FA_LDS* stage1 = (char FA_LDS*)stage1_raw;
+  constexpr int OPS = 2 * RC::PER_WAVE;
+  __shared__ __attribute__((aligned(1024))) char s0_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s1_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s2_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s3_raw[S::BYTES];
+  char FA_LDS* const stg[NSTAGE] = {(char FA_LDS*)s0_raw, (char FA_LDS*)s1_raw, (char FA_LDS*)s2_raw,
+                                    (char FA_LDS*)s3_raw};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
   int w = blockIdx.x;
@@ -381,14 +565,9 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   const char* kbase = (const char*)p.k + ((long)seq0 * p.Hkv + hkv) * D * 2;
   const char* vbase = (const char*)p.v + ((long)seq0 * p.Hkv + hkv) * D * 2;
   const int kv_end = CAUSAL ? min(L, q0 + Q_BM) : L;
-  const int n_kv = (kv_end + Q_BN - 1) / Q_BN;
+  const int n_it = (kv_end + TROWS - 1) / TROWS;
 
-  auto issue = [&](int kt, char FA_LDS* stage) {
-    load_rows<D, Q_BN>(stage, kbase, kv_stride_b, kt * Q_BN, L, wave, lane);
-    load_rows<D, Q_BN>(stage + S::TILEB, vbase, kv_stride_b, kt * Q_BN, L, wave, lane);
-  };
-  issue(0, stage0);
-
+  // ---- Q, dO fragments of this lane's query (B operands), its LSE2 and D ----
   bf16x8 qf[KSTEPS], of[KSTEPS];
   float lse2, dq_d;
   {
@@ -401,85 +580,151 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
       of[ks] = *(const bf16x8*)(op + ks * 16);
     }
     const long li = lse_index(p, s, h, seq0, qr, T, VARLEN);
-    lse2 = p.lse[li] * kLog2e;
+    lse2 = p.lse2[li];
     dq_d = p.dsum[li];
   }
+
+  RC copy;
+  copy.init(wave, lane, (unsigned)kv_stride_b);
+  int iss = 0;
+  auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
+    copy.issue(stage, kbase, kv_stride_b, iss * TROWS, L);
+    copy.issue(stage + S::TILEB, vbase, kv_stride_b, iss * TROWS, L);
+    ++iss;
+  };
+  issue_next(stg[0]);
+  if (n_it > 1) issue_next(stg[1]);
+  if (n_it > 2) issue_next(stg[2]);
+
+  TileOffsets<D> to;
+  to.init(lane);
   f32x16 dq[DBLK];
 #pragma unroll
   for (int i = 0; i < DBLK; ++i) dq[i] = f32x16{};
+  f32x16 sA[2], pA[2], sB[2], pB[2];             // S^T, dP^T of two consecutive tiles
+  u32x4 dsb[4];                                  // dS^T (bf16 pairs) of the current tile
   const float c = p.scale_log2;
 
-  wait_vmem();
-  __syncthreads();
-  const int g16 = lane & 15;
-  auto step = [&](char FA_LDS* cur, char FA_LDS* nxt, const int kt) __attribute__((always_inline)) {
-    if (kt + 1 < n_kv) issue(kt + 1, nxt);
-    const int k0 = kt * Q_BN;
-    const bool active = !CAUSAL || (k0 <= qw0 + 31);
-    if (active) {
-      const char FA_LDS* ktile = cur;
-      const char FA_LDS* vtile = cur + S::TILEB;
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      f32x16 pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + l32;
-          const int off = row * S::ROWB + (((2 * ks + hl) ^ lds_swz<D>(row)) * 16);
-          sacc[kb] = mfma32(lds_read16(ktile + off), qf[ks], sacc[kb]);
-          pacc[kb] = mfma32(lds_read16(vtile + off), of[ks], pacc[kb]);
-        }
-      }
-      const bool need_mask = (k0 + Q_BN > L) || (CAUSAL && (k0 + Q_BN - 1 > qw0));
-      bf16x8 db8[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 b;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float d2[2];
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-              const int r = 8 * half + e + z;
-              float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -lse2));
-              if (need_mask) {
-                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                const bool dead = (key >= L) || (CAUSAL && key > my_q);
-                pe = dead ? 0.f : pe;
-              }
-              d2[z] = pe * (pacc[kb][r] - dq_d);
-            }
-            const bf16x2 t2 = pack_bf16(d2[0], d2[1]);
-            b[e] = t2[0];
-            b[e + 1] = t2[1];
-          }
-          db8[kb * 2 + half] = b;
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r0 = 16 * t + 4 * hl + (g16 >> 2), r1 = r0 + 8;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int dcol = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
-          const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
-          const int o0 = r0 * S::ROWB + ((chunk ^ lds_swz<D>(r0)) * 16) + sub;
-          const int o1 = r1 * S::ROWB + ((chunk ^ lds_swz<D>(r1)) * 16) + sub;
-          dq[db] = mfma32(cat(lds_read_tr(ktile + o0), lds_read_tr(ktile + o1)), db8[t], dq[db]);
-        }
-      }
-    }
-    wait_vmem();
-    __syncthreads();
+  constexpr int NA = 4 * KSTEPS;
+  auto a_fetch = [&](const char FA_LDS* tile, int j) __attribute__((always_inline)) {
+    const int ks = j >> 2, cc = j & 3;
+    return to.row_operand(tile + (cc >> 1) * S::TILEB, ks, cc & 1);
   };
-  for (int kt = 0; kt < n_kv; kt += 2) {
-    step(stage0, stage1, kt);
-    if (kt + 1 < n_kv) step(stage1, stage0, kt + 1);
+  auto a_step = [&](f32x16 (&sx)[2], f32x16 (&px)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
+    const int ks = j >> 2, cc = j & 3;
+    f32x16& acc = cc < 2 ? sx[cc & 1] : px[cc & 1];
+    const bf16x8& b = cc < 2 ? qf[ks] : of[ks];
+    if (ks == 0) mfma_v_first(acc, a, b);
+    else mfma_v(acc, a, b);
+  };
+  auto phase_a0 = [&](const char FA_LDS* tile, f32x16 (&sx)[2], f32x16 (&px)[2]) __attribute__((always_inline)) {
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(tile, i);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const bf16x8 a = qa[j % PF];
+      if (j + PF < NA) qa[j % PF] = a_fetch(tile, j + PF);
+      a_step(sx, px, j, a);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Element e of the current tile: key block kb = e / 16, register r = e % 16,
+  // key k0 + kb*32 + 8(r/4) + 4 hl + r%4, query = this lane's query.
+  auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, f32x16 (&sx)[2], f32x16 (&px)[2],
+                     const f32x16 (&sc)[2], const f32x16 (&pc)[2], int k0) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int EPS = 32 / NA;
+    float dv2[2];
+    auto elem = [&](int e) __attribute__((always_inline)) {
+      const int kb = e >> 4, r = e & 15;
+      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -lse2));
+      if constexpr (MASK) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool dead = (key >= L) || (CAUSAL && key > my_q);
+        pe = dead ? 0.f : pe;
+      }
+      dv2[e & 1] = pe * (pc[kb][r] - dq_d);
+      if (e & 1) {
+        const int t = kb * 2 + (r >> 3), pos = (r & 7) >> 1;
+        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
+      }
+    };
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(nt, i);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const bf16x8 a = qa[j % PF];
+      if (j + PF < NA) qa[j % PF] = a_fetch(nt, j + PF);
+      a_step(sx, px, j, a);
+#pragma unroll
+      for (int x = 0; x < EPS; ++x) elem(j * EPS + x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Phase B: dQ^T += K^T dS^T; step i: key step t = i / DBLK, d-block db = i % DBLK.
+  constexpr int NB = 4 * DBLK;
+  auto phase_b = [&](const char FA_LDS* ct) __attribute__((always_inline)) {
+    auto fetch = [&](int i) __attribute__((always_inline)) { return to.tr_operand(ct, i / DBLK, i % DBLK); };
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = fetch(i);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 2");   // VALU-written B operands -> first MFMA
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const bf16x8 a = qa[i % PF];
+      if (i + PF < NB) qa[i % PF] = fetch(i + PF);
+      mfma_a(dq[i % DBLK], a, __builtin_bit_cast(bf16x8, dsb[i / DBLK]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (n_it > 2) wait_vm(2 * OPS);
+  else if (n_it > 1) wait_vm(OPS);
+  else wait_vm(0);
+  barrier_no_fence();
+  phase_a0(stg[0], sA, pA);
+  mfma_result_wait();
+
+  auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
+    constexpr int BI = decltype(bi_tag)::value;
+    if (i + 2 < n_it) wait_vm(OPS);
+    else if (i + 1 < n_it) wait_vm(0);
+    barrier_no_fence();
+    if (i + 3 < n_it) issue_next(stg[(BI + 3) % NSTAGE]);
+    const int k0 = i * TROWS;
+    const bool need_mask = (k0 + TROWS > L) || (CAUSAL && k0 + TROWS - 1 > qw0);
+    if constexpr (BI % 2 == 0) {
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
+    } else {
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], sA, pA, sB, pB, k0);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], sA, pA, sB, pB, k0);
+    }
+    phase_b(stg[BI]);
+  };
+  for (int i = 0; i < n_it; i += NSTAGE) {
+    iter(ic<0>{}, i);
+    if (i + 1 < n_it) iter(ic<1>{}, i + 1);
+    if (i + 2 < n_it) iter(ic<2>{}, i + 2);
+    if (i + 3 < n_it) iter(ic<3>{}, i + 3);
   }
-  char FA_LDS* st = (wave < 2 ? stage0 : stage1) + (wave & 1) * 32 * S::OROWB;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    keep_live(sA[x]);
+    keep_live(pA[x]);
+    keep_live(sB[x]);
+    keep_live(pB[x]);
+  }
+  mfma_result_wait();
+
+  barrier_no_fence();
+  char FA_LDS* st = stg[0];
+  if (wave == 1) st = stg[1];
+  if (wave == 2) st = stg[2];
+  if (wave == 3) st = stg[3];
   __bf16* dqb = (__bf16*)p.dq + ((long)seq0 * p.Hq + h) * D;
   store_rows_bf16<D>(st, dq, p.scale, dqb, q_stride, qw0, L, lane);
 }
@@ -493,7 +738,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t strea
   if (stages & 1) {
     const long rows = (long)p.B * p.N * p.Hq;    // upper bound (packed: T <= B * N)
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_dsum_kernel<D, VARLEN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_prep_kernel<D, VARLEN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        stream, p, rows);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

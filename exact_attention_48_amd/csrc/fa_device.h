@@ -34,6 +34,30 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same MFMA with the register file of each operand fixed by inline asm
+// (the compiler would otherwise put every accumulator in AGPRs and copy the
+// ones the VALU reads back every tile). The compiler does not see these as
+// MFMAs, so their users keep the hazard rules themselves: a VALU write of an
+// operand is followed by at least 2 other instructions before the MFMA that
+// reads it, and an MFMA result is not read or overwritten by the VALU within
+// 19 wait states of the MFMA (mfma_result_wait() pads where nothing else does).
+//   acc (VGPR) = A * B (accumulator start 0), B held in AGPRs
+__device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+//   acc (VGPR) += A * B, B held in AGPRs
+__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+//   acc (AGPR) += A * B, A and B in VGPRs
+__device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory"); }
+// Keeps an asm MFMA result allocated up to this point (a result that is never
+// read would otherwise free its registers while the MFMA still writes them).
+__device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
+
 // Both lanes of the pair (l, l ^ 32) receive max(x[l], x[l ^ 32]).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -37,6 +37,7 @@ struct BwdParams {
   void* dv;
   const int32_t* cu_seqlens;
   float* dsum;                 // workspace: D_i = rowsum(dO * O), laid out like LSE
+  float* lse2;                 // workspace: LSE_i * log2(e), laid out like LSE
   int B, Hq, Hkv, G, N;
   float scale;
   float scale_log2;
