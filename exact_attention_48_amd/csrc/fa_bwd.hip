@@ -372,6 +372,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
                      f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int q0)
                      __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // distinct first instructions keep the compiler from hoisting the code the
+    // masked and unmasked variants share above their branch (which would
+    // compute all 32 elements' operands at once)
+    if constexpr (MASK) asm volatile("; masked tile");
+    else asm volatile("; unmasked tile");
     constexpr int EPS = 32 / NA;                 // softmax elements per MFMA slot
     const float FA_LDS* lz = (const float FA_LDS*)(ct + S::LSEOFF + lse_lane);
     const float FA_LDS* dz = lz + TROWS;
@@ -634,10 +639,19 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, f32x16 (&sx)[2], f32x16 (&px)[2],
                      const f32x16 (&sc)[2], const f32x16 (&pc)[2], int k0) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // distinct first instructions keep the compiler from hoisting the code the
+    // masked and unmasked variants share above their branch (which would
+    // compute all 32 elements' operands at once)
+    if constexpr (MASK) asm volatile("; masked tile");
+    else asm volatile("; unmasked tile");
     constexpr int EPS = 32 / NA;
     float dv2[2];
     auto elem = [&](int e) __attribute__((always_inline)) {
       const int kb = e >> 4, r = e & 15;
+      // lse2 and dq_d are "redefined" (no instruction) at every element so the
+      // element's arithmetic stays in its MFMA slot instead of being hoisted
+      // to the top of the phase, where all 32 results would be live at once
+      asm volatile("" : "+v"(lse2), "+v"(dq_d));
       float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -lse2));
       if constexpr (MASK) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
