@@ -50,21 +50,20 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int NSTAGE = 4;     // LDS ring depth
 constexpr int TROWS = 64;     // rows per streamed tile (Q/dO or K/V)
 constexpr int KV_BN = 128;    // keys per dK/dV workgroup (32 per wave)
-constexpr int Q_BM = 128;     // queries per dQ workgroup (32 per wave)
 constexpr int PF = 4;         // MFMA operands read ahead
 
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-// HBM -> LDS copy of a TROWS x D bf16 tile of a [tokens][stride] tensor into a
+// HBM -> LDS copy of a ROWS x D bf16 tile of a [tokens][stride] tensor into a
 // swizzled LDS tile; rows past the sequence end are clamped to its last row.
 // All NWAVES waves take part, PER_WAVE 1 KiB instructions each.
-template <int D>
+template <int D, int ROWS>
 struct RowCopy {
   static constexpr int ROWB = D * 2;
   static constexpr int LPR = ROWB / 16;          // lanes per row
   static constexpr int RPI = 64 / LPR;           // rows per instruction
-  static constexpr int NI = TROWS / RPI;         // instructions per tile
+  static constexpr int NI = ROWS / RPI;          // instructions per tile
   static constexpr int PER_WAVE = NI / NWAVES;
   static_assert(PER_WAVE * NWAVES == NI, "tile copy must split evenly over the waves");
   unsigned off[PER_WAVE];                        // row * stride + swizzled chunk * 16
@@ -80,11 +79,11 @@ struct RowCopy {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) off[u] = (unsigned)row(u) * stride + chunk16(u);
   }
-  // `base` points at token 0 of this head; rows r0 .. r0 + TROWS - 1.
+  // `base` points at token 0 of this head; rows r0 .. r0 + ROWS - 1.
   __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int r0, int L) const {
     const char* tb = base + (long)r0 * stride;
     char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
-    if (r0 + TROWS <= L) {
+    if (r0 + ROWS <= L) {
 #pragma unroll
       for (int u = 0; u < PER_WAVE; ++u) {
         unsigned o = off[u];
@@ -234,7 +233,7 @@ template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const BwdParams p) {
   using S = KvStage<D>;
-  using RC = RowCopy<D>;
+  using RC = RowCopy<D, TROWS>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int ROWB = S::ROWB;
@@ -509,20 +508,28 @@ void bwd_dkdv_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // 3. dQ: Q-major
 // ---------------------------------------------------------------------------
+// Each wave owns 64 queries (two 32-query MFMA blocks), so every K / V / K^T
+// fragment read from LDS feeds two MFMAs; the waves' Q and dO fragments and
+// dQ accumulators fill the accumulation registers. K/V stream in 32-key tiles
+// through the 4-stage ring (4 x 16 KiB for d = 128).
+constexpr int DQ_WQ = 64;                 // queries per wave
+constexpr int DQ_BM = NWAVES * DQ_WQ;     // queries per workgroup
+constexpr int DQ_BN = 32;                 // keys per K/V tile
+
 template <int D>
 struct QStage {
   static constexpr int ROWB = D * 2;
-  static constexpr int TILEB = TROWS * ROWB;          // one K or V tile
+  static constexpr int TILEB = DQ_BN * ROWB;          // one K or V tile
   static constexpr int BYTES = 2 * TILEB;
   static constexpr int OROWB = ROWB + 16;
-  static_assert(32 * OROWB <= BYTES, "a wave's output staging must fit in one stage");
+  static_assert(32 * OROWB <= BYTES, "32 rows of a wave's output staging must fit in one stage");
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   using S = QStage<D>;
-  using RC = RowCopy<D>;
+  using RC = RowCopy<D, DQ_BN>;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int OPS = 2 * RC::PER_WAVE;
@@ -560,41 +567,44 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
     seq0 = s * p.N;
     L = p.N;
   }
-  const int q0 = qt * Q_BM;
+  const int q0 = qt * DQ_BM;
   if (q0 >= L) return;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
+  const int qw0 = q0 + wave * DQ_WQ;            // first query of this wave
+  int my_q[2];
+  my_q[0] = qw0 + l32;
+  my_q[1] = qw0 + 32 + l32;
 
   const long q_stride = (long)p.Hq * D;
   const long kv_stride_b = (long)p.Hkv * D * 2;
   const char* kbase = (const char*)p.k + ((long)seq0 * p.Hkv + hkv) * D * 2;
   const char* vbase = (const char*)p.v + ((long)seq0 * p.Hkv + hkv) * D * 2;
-  const int kv_end = CAUSAL ? min(L, q0 + Q_BM) : L;
-  const int n_it = (kv_end + TROWS - 1) / TROWS;
+  const int kv_end = CAUSAL ? min(L, q0 + DQ_BM) : L;
+  const int n_it = (kv_end + DQ_BN - 1) / DQ_BN;
 
-  // ---- Q, dO fragments of this lane's query (B operands), its LSE2 and D ----
-  bf16x8 qf[KSTEPS], of[KSTEPS];
-  float lse2, dq_d;
-  {
-    const int qr = my_q < L ? my_q : L - 1;
+  // ---- Q, dO fragments of this lane's two queries (B operands), LSE2 and D ----
+  bf16x8 qf[2][KSTEPS], of[2][KSTEPS];
+  float lse2[2], dq_d[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = my_q[qb] < L ? my_q[qb] : L - 1;
     const __bf16* qp = (const __bf16*)p.q + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 8;
     const __bf16* op = (const __bf16*)p.dout + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      qf[ks] = *(const bf16x8*)(qp + ks * 16);
-      of[ks] = *(const bf16x8*)(op + ks * 16);
+      qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
+      of[qb][ks] = *(const bf16x8*)(op + ks * 16);
     }
     const long li = lse_index(p, s, h, seq0, qr, T, VARLEN);
-    lse2 = p.lse2[li];
-    dq_d = p.dsum[li];
+    lse2[qb] = p.lse2[li];
+    dq_d[qb] = p.dsum[li];
   }
 
   RC copy;
   copy.init(wave, lane, (unsigned)kv_stride_b);
   int iss = 0;
   auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
-    copy.issue(stage, kbase, kv_stride_b, iss * TROWS, L);
-    copy.issue(stage + S::TILEB, vbase, kv_stride_b, iss * TROWS, L);
+    copy.issue(stage, kbase, kv_stride_b, iss * DQ_BN, L);
+    copy.issue(stage + S::TILEB, vbase, kv_stride_b, iss * DQ_BN, L);
     ++iss;
   };
   issue_next(stg[0]);
@@ -603,82 +613,89 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
 
   TileOffsets<D> to;
   to.init(lane);
-  f32x16 dq[DBLK];
+  f32x16 dq[2][DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i) dq[i] = f32x16{};
-  f32x16 sA[2], pA[2], sB[2], pB[2];             // S^T, dP^T of two consecutive tiles
-  u32x4 dsb[4];                                  // dS^T (bf16 pairs) of the current tile
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) dq[qb][i] = f32x16{};
+  f32x16 sA[2], pA[2], sB[2], pB[2];             // S^T, dP^T of a tile, per query block, two tiles
+  u32x4 dsb[2][2];                               // dS^T (bf16 pairs) of the current tile [query block][key step]
   const float c = p.scale_log2;
 
+  // Phase-A MFMA j: k-step j / 4, operand j % 4 = S block 0, S block 1, dP block
+  // 0, dP block 1. The K (or V) fragment of a k-step serves both query blocks,
+  // so fragment f = j / 2 is read once: k-step f / 2 of K (f even) or V.
   constexpr int NA = 4 * KSTEPS;
-  auto a_fetch = [&](const char FA_LDS* tile, int j) __attribute__((always_inline)) {
-    const int ks = j >> 2, cc = j & 3;
-    return to.row_operand(tile + (cc >> 1) * S::TILEB, ks, cc & 1);
+  constexpr int NF = NA / 2;
+  auto a_frag = [&](const char FA_LDS* tile, int f) __attribute__((always_inline)) {
+    return to.row_operand(tile + (f & 1) * S::TILEB, f >> 1, 0);
   };
   auto a_step = [&](f32x16 (&sx)[2], f32x16 (&px)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
     const int ks = j >> 2, cc = j & 3;
     f32x16& acc = cc < 2 ? sx[cc & 1] : px[cc & 1];
-    const bf16x8& b = cc < 2 ? qf[ks] : of[ks];
+    const bf16x8& b = cc < 2 ? qf[cc & 1][ks] : of[cc & 1][ks];
     if (ks == 0) mfma_v_first(acc, a, b);
     else mfma_v(acc, a, b);
   };
   auto phase_a0 = [&](const char FA_LDS* tile, f32x16 (&sx)[2], f32x16 (&px)[2]) __attribute__((always_inline)) {
     bf16x8 qa[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(tile, i);
+    for (int i = 0; i < PF; ++i) qa[i] = a_frag(tile, i);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const bf16x8 a = qa[j % PF];
-      if (j + PF < NA) qa[j % PF] = a_fetch(tile, j + PF);
-      a_step(sx, px, j, a);
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8 a = qa[f % PF];
+      if (f + PF < NF) qa[f % PF] = a_frag(tile, f + PF);
+      a_step(sx, px, 2 * f, a);
+      a_step(sx, px, 2 * f + 1, a);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Element e of the current tile: key block kb = e / 16, register r = e % 16,
-  // key k0 + kb*32 + 8(r/4) + 4 hl + r%4, query = this lane's query.
+  // Element e of the current tile: query block qb = e / 16, register r = e % 16,
+  // key k0 + 8(r/4) + 4 hl + r%4, query my_q[qb].
   auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, f32x16 (&sx)[2], f32x16 (&px)[2],
                      const f32x16 (&sc)[2], const f32x16 (&pc)[2], int k0) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // distinct first instructions keep the compiler from hoisting the code the
-    // masked and unmasked variants share above their branch (which would
-    // compute all 32 elements' operands at once)
+    // masked and unmasked variants share above their branch
     if constexpr (MASK) asm volatile("; masked tile");
     else asm volatile("; unmasked tile");
     constexpr int EPS = 32 / NA;
     float dv2[2];
     auto elem = [&](int e) __attribute__((always_inline)) {
-      const int kb = e >> 4, r = e & 15;
+      const int qb = e >> 4, r = e & 15;
       // lse2 and dq_d are "redefined" (no instruction) at every element so the
       // element's arithmetic stays in its MFMA slot instead of being hoisted
       // to the top of the phase, where all 32 results would be live at once
-      asm volatile("" : "+v"(lse2), "+v"(dq_d));
-      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -lse2));
+      asm volatile("" : "+v"(lse2[qb]), "+v"(dq_d[qb]));
+      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][r], c, -lse2[qb]));
       if constexpr (MASK) {
-        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool dead = (key >= L) || (CAUSAL && key > my_q);
+        const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool dead = (key >= L) || (CAUSAL && key > my_q[qb]);
         pe = dead ? 0.f : pe;
       }
-      dv2[e & 1] = pe * (pc[kb][r] - dq_d);
-      if (e & 1) {
-        const int t = kb * 2 + (r >> 3), pos = (r & 7) >> 1;
-        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
-      }
+      dv2[e & 1] = pe * (pc[qb][r] - dq_d[qb]);
+      if (e & 1) dsb[qb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
     };
     bf16x8 qa[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) qa[i] = a_fetch(nt, i);
+    for (int i = 0; i < PF; ++i) qa[i] = a_frag(nt, i);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const bf16x8 a = qa[j % PF];
-      if (j + PF < NA) qa[j % PF] = a_fetch(nt, j + PF);
-      a_step(sx, px, j, a);
+    for (int f = 0; f < NF; ++f) {
+      const bf16x8 a = qa[f % PF];
+      if (f + PF < NF) qa[f % PF] = a_frag(nt, f + PF);
 #pragma unroll
-      for (int x = 0; x < EPS; ++x) elem(j * EPS + x);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int x = 0; x < 2; ++x) {
+        const int j = 2 * f + x;
+        a_step(sx, px, j, a);
+#pragma unroll
+        for (int y = 0; y < EPS; ++y) elem(j * EPS + y);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
-  // Phase B: dQ^T += K^T dS^T; step i: key step t = i / DBLK, d-block db = i % DBLK.
-  constexpr int NB = 4 * DBLK;
+  // Phase B: dQ^T += K^T dS^T. Fragment i: key step t = i / DBLK, d-block
+  // db = i % DBLK, used by both query blocks.
+  constexpr int NB = 2 * DBLK;
   auto phase_b = [&](const char FA_LDS* ct) __attribute__((always_inline)) {
     auto fetch = [&](int i) __attribute__((always_inline)) { return to.tr_operand(ct, i / DBLK, i % DBLK); };
     bf16x8 qa[PF];
@@ -690,7 +707,9 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
     for (int i = 0; i < NB; ++i) {
       const bf16x8 a = qa[i % PF];
       if (i + PF < NB) qa[i % PF] = fetch(i + PF);
-      mfma_a(dq[i % DBLK], a, __builtin_bit_cast(bf16x8, dsb[i / DBLK]));
+      const int t = i / DBLK, db = i % DBLK;
+      mfma_a(dq[0][db], a, __builtin_bit_cast(bf16x8, dsb[0][t]));
+      mfma_a(dq[1][db], a, __builtin_bit_cast(bf16x8, dsb[1][t]));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -702,14 +721,19 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   phase_a0(stg[0], sA, pA);
   mfma_result_wait();
 
+  // Iteration i (BI = i % NSTAGE): tile i in stg[BI], tile i+1 in stg[BI+1],
+  // tile i+3 is copied into stg[BI+3] (last read as tile i-1, before this
+  // iteration's barrier).
   auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
     constexpr int BI = decltype(bi_tag)::value;
     if (i + 2 < n_it) wait_vm(OPS);
     else if (i + 1 < n_it) wait_vm(0);
     barrier_no_fence();
     if (i + 3 < n_it) issue_next(stg[(BI + 3) % NSTAGE]);
-    const int k0 = i * TROWS;
-    const bool need_mask = (k0 + TROWS > L) || (CAUSAL && k0 + TROWS - 1 > qw0);
+    const int k0 = i * DQ_BN;
+    const bool need_mask = (k0 + DQ_BN > L) || (CAUSAL && k0 + DQ_BN - 1 > qw0);
+    // the S/dP MFMAs of tile i+1 also run on the last iteration (on stale LDS,
+    // results unused) so that the code has a single shape
     if constexpr (BI % 2 == 0) {
       if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
       else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
@@ -740,7 +764,10 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   if (wave == 2) st = stg[2];
   if (wave == 3) st = stg[3];
   __bf16* dqb = (__bf16*)p.dq + ((long)seq0 * p.Hq + h) * D;
-  store_rows_bf16<D>(st, dq, p.scale, dqb, q_stride, qw0, L, lane);
+  store_rows_bf16<D>(st, dq[0], p.scale, dqb, q_stride, qw0, L, lane);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  store_rows_bf16<D>(st, dq[1], p.scale, dqb, q_stride, qw0 + 32, L, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -763,7 +790,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t strea
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {
-    const int n_qt = (p.N + Q_BM - 1) / Q_BM;
+    const int n_qt = (p.N + DQ_BM - 1) / DQ_BM;
     const int items = n_qt * p.B * p.Hq;
     const int xg = p.G;
     const int grid = (items + 8 * xg - 1) / (8 * xg) * (8 * xg);
