@@ -367,9 +367,17 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // softmax of the current tile (`ct`, rows q0.., S/dP in sc/pc) -> pb, dsb.
   // Element e of the current tile: block qb = e / 16, register r = e % 16,
   // query row qb*32 + 8(r/4) + 4 hl + r%4, key = this lane's key.
+  // The copy of a later tile (`issue`) goes out right after the first operand
+  // reads; the last PF slots also read the first PF transposed operands of
+  // phase B (`pre`).
+  constexpr int NB = 8 * DBLK;
+  auto b_fetch = [&](const char FA_LDS* ct, int i) __attribute__((always_inline)) {
+    const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
+    return to.tr_operand(ct + ((i & 1) ? 0 : S::TILEB), t, db);
+  };
   auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2],
-                     f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int q0)
-                     __attribute__((always_inline)) {
+                     f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int q0, bool issue,
+                     char FA_LDS* issue_stage, bf16x8 (&pre)[PF]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // distinct first instructions keep the compiler from hoisting the code the
     // masked and unmasked variants share above their branch (which would
@@ -403,14 +411,17 @@ void bwd_dkdv_kernel(const BwdParams p) {
         dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
       }
     };
-    g_fetch(0);
     bf16x8 qa[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) qa[i] = a_fetch(nt, i);
+    if (issue) issue_next(issue_stage);
+    g_fetch(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const bf16x8 a = qa[j % PF];
       if (j + PF < NA) qa[j % PF] = a_fetch(nt, j + PF);
+      else pre[j + PF - NA] = b_fetch(ct, j + PF - NA);
       a_step(sx, px, j, a);
 #pragma unroll
       for (int x = 0; x < EPS; ++x) elem(j * EPS + x);
@@ -420,21 +431,13 @@ void bwd_dkdv_kernel(const BwdParams p) {
 
   // Phase B: dV^T += dO^T P, dK^T += Q^T dS for the current tile. Step i:
   // key step t = i / (2 DBLK), d-block db = (i / 2) % DBLK, dV (even i) or dK.
-  constexpr int NB = 8 * DBLK;
-  auto phase_b = [&](const char FA_LDS* ct) __attribute__((always_inline)) {
-    auto fetch = [&](int i) __attribute__((always_inline)) {
-      const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
-      return to.tr_operand(ct + ((i & 1) ? 0 : S::TILEB), t, db);
-    };
-    bf16x8 qa[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) qa[i] = fetch(i);
-    __builtin_amdgcn_sched_barrier(0);
+  // `qa` holds the operands of steps 0 .. PF-1 (read during phase A).
+  auto phase_b = [&](const char FA_LDS* ct, bf16x8 (&qa)[PF]) __attribute__((always_inline)) {
     asm volatile("s_nop 2");   // VALU-written B operands -> first MFMA
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const bf16x8 a = qa[i % PF];
-      if (i + PF < NB) qa[i % PF] = fetch(i + PF);
+      if (i + PF < NB) qa[i % PF] = b_fetch(ct, i + PF);
       const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
       if (i & 1) mfma_a(dk[db], a, __builtin_bit_cast(bf16x8, dsb[t]));
       else mfma_a(dv[db], a, __builtin_bit_cast(bf16x8, pb[t]));
@@ -459,20 +462,22 @@ void bwd_dkdv_kernel(const BwdParams p) {
     if (i + 2 < n_it) wait_vm(OPS);
     else if (i + 1 < n_it) wait_vm(0);
     barrier_no_fence();
-    if (i + 3 < n_it) issue_next(stg[(BI + 3) % NSTAGE]);
+    const bool issue = i + 3 < n_it;
+    char FA_LDS* const nst = stg[(BI + 3) % NSTAGE];
     const int q0 = cur_qt * TROWS;
     if (++cur_qt == n_qt) cur_qt = qt0;
     const bool need_mask = (q0 + TROWS > L) || (CAUSAL && kw0 + 31 > q0);
     // the S/dP MFMAs of tile i+1 also run on the last iteration (on stale LDS,
     // results unused) so that the code has a single shape
+    bf16x8 pre[PF];
     if constexpr (BI % 2 == 0) {
-      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0);
-      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0);
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0, issue, nst, pre);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0, issue, nst, pre);
     } else {
-      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0);
-      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0);
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0, issue, nst, pre);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0, issue, nst, pre);
     }
-    phase_b(stg[BI]);
+    phase_b(stg[BI], pre);
   };
   for (int i = 0; i < n_it; i += NSTAGE) {
     iter(ic<0>{}, i);
@@ -652,8 +657,16 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   };
   // Element e of the current tile: query block qb = e / 16, register r = e % 16,
   // key k0 + 8(r/4) + 4 hl + r%4, query my_q[qb].
-  auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, f32x16 (&sx)[2], f32x16 (&px)[2],
-                     const f32x16 (&sc)[2], const f32x16 (&pc)[2], int k0) __attribute__((always_inline)) {
+  // The copy of a later tile (`issue`) goes out right after the first operand
+  // reads; the last PF fragment slots also read the first PF transposed
+  // fragments of phase B (`pre`, from the current tile `ct`).
+  constexpr int NB = 2 * DBLK;
+  auto b_fetch = [&](const char FA_LDS* ct, int i) __attribute__((always_inline)) {
+    return to.tr_operand(ct, i / DBLK, i % DBLK);
+  };
+  auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2],
+                     f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int k0, bool issue,
+                     char FA_LDS* issue_stage, bf16x8 (&pre)[PF]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // distinct first instructions keep the compiler from hoisting the code the
     // masked and unmasked variants share above their branch
@@ -679,10 +692,13 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
     bf16x8 qa[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) qa[i] = a_frag(nt, i);
+    if (issue) issue_next(issue_stage);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const bf16x8 a = qa[f % PF];
       if (f + PF < NF) qa[f % PF] = a_frag(nt, f + PF);
+      else if (f + PF - NF < NB) pre[f + PF - NF] = b_fetch(ct, f + PF - NF);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int j = 2 * f + x;
@@ -694,19 +710,14 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
     }
   };
   // Phase B: dQ^T += K^T dS^T. Fragment i: key step t = i / DBLK, d-block
-  // db = i % DBLK, used by both query blocks.
-  constexpr int NB = 2 * DBLK;
-  auto phase_b = [&](const char FA_LDS* ct) __attribute__((always_inline)) {
-    auto fetch = [&](int i) __attribute__((always_inline)) { return to.tr_operand(ct, i / DBLK, i % DBLK); };
-    bf16x8 qa[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) qa[i] = fetch(i);
-    __builtin_amdgcn_sched_barrier(0);
+  // db = i % DBLK, used by both query blocks; `qa` holds fragments 0 .. PF-1.
+  static_assert(PF <= NB, "phase B must have at least PF fragments");
+  auto phase_b = [&](const char FA_LDS* ct, bf16x8 (&qa)[PF]) __attribute__((always_inline)) {
     asm volatile("s_nop 2");   // VALU-written B operands -> first MFMA
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const bf16x8 a = qa[i % PF];
-      if (i + PF < NB) qa[i % PF] = fetch(i + PF);
+      if (i + PF < NB) qa[i % PF] = b_fetch(ct, i + PF);
       const int t = i / DBLK, db = i % DBLK;
       mfma_a(dq[0][db], a, __builtin_bit_cast(bf16x8, dsb[0][t]));
       mfma_a(dq[1][db], a, __builtin_bit_cast(bf16x8, dsb[1][t]));
@@ -729,19 +740,21 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
     if (i + 2 < n_it) wait_vm(OPS);
     else if (i + 1 < n_it) wait_vm(0);
     barrier_no_fence();
-    if (i + 3 < n_it) issue_next(stg[(BI + 3) % NSTAGE]);
+    const bool issue = i + 3 < n_it;
+    char FA_LDS* const nst = stg[(BI + 3) % NSTAGE];
     const int k0 = i * DQ_BN;
     const bool need_mask = (k0 + DQ_BN > L) || (CAUSAL && k0 + DQ_BN - 1 > qw0);
     // the S/dP MFMAs of tile i+1 also run on the last iteration (on stale LDS,
     // results unused) so that the code has a single shape
+    bf16x8 pre[PF];
     if constexpr (BI % 2 == 0) {
-      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
-      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], sB, pB, sA, pA, k0);
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, k0, issue, nst, pre);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, k0, issue, nst, pre);
     } else {
-      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], sA, pA, sB, pB, k0);
-      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], sA, pA, sB, pB, k0);
+      if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, k0, issue, nst, pre);
+      else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, k0, issue, nst, pre);
     }
-    phase_b(stg[BI]);
+    phase_b(stg[BI], pre);
   };
   for (int i = 0; i < n_it; i += NSTAGE) {
     iter(ic<0>{}, i);
