@@ -40,143 +40,19 @@
 
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tiles.h"
 
 namespace fa {
 
+using namespace tiles;
+
 namespace {
 
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int NSTAGE = 4;     // LDS ring depth
 constexpr int TROWS = 64;     // rows per streamed tile (Q/dO or K/V)
 constexpr int KV_BN = 128;    // keys per dK/dV workgroup (32 per wave)
-constexpr int PF = 4;         // MFMA operands read ahead
-
-template <int N>
-using ic = std::integral_constant<int, N>;
-
-// HBM -> LDS copy of a ROWS x D bf16 tile of a [tokens][stride] tensor into a
-// swizzled LDS tile; rows past the sequence end are clamped to its last row.
-// All NWAVES waves take part, PER_WAVE 1 KiB instructions each.
-template <int D, int ROWS>
-struct RowCopy {
-  static constexpr int ROWB = D * 2;
-  static constexpr int LPR = ROWB / 16;          // lanes per row
-  static constexpr int RPI = 64 / LPR;           // rows per instruction
-  static constexpr int NI = ROWS / RPI;          // instructions per tile
-  static constexpr int PER_WAVE = NI / NWAVES;
-  static_assert(PER_WAVE * NWAVES == NI, "tile copy must split evenly over the waves");
-  unsigned off[PER_WAVE];                        // row * stride + swizzled chunk * 16
-  int wave, lane;
-
-  __device__ __forceinline__ int row(int u) const { return (wave * PER_WAVE + u) * RPI + lane / LPR; }
-  __device__ __forceinline__ unsigned chunk16(int u) const {
-    return (unsigned)(((lane % LPR) ^ lds_swz<D>(row(u))) * 16);
-  }
-  __device__ __forceinline__ void init(int wave_, int lane_, unsigned stride) {
-    wave = wave_;
-    lane = lane_;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) off[u] = (unsigned)row(u) * stride + chunk16(u);
-  }
-  // `base` points at token 0 of this head; rows r0 .. r0 + ROWS - 1.
-  __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int r0, int L) const {
-    const char* tb = base + (long)r0 * stride;
-    char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
-    if (r0 + ROWS <= L) {
-#pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        unsigned o = off[u];
-        asm volatile("" : "+v"(o));   // keep the 64-bit address out of loop-invariant code motion
-        g2lds16(tb + o, dst + u * 1024);
-      }
-    } else {
-      const int last = L - 1 - r0;
-#pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        const int r = min(row(u), last);
-        g2lds16(tb + ((unsigned)r * (unsigned)stride + chunk16(u)), dst + u * 1024);
-      }
-    }
-  }
-};
 
 __device__ __forceinline__ long lse_index(const BwdParams& p, int s, int h, int seq0, int row, int T, bool varlen) {
   return varlen ? (long)h * T + seq0 + row : ((long)s * p.Hq + h) * p.N + row;
-}
-
-// Per-lane LDS offsets of the MFMA operands in a swizzled [64][D] bf16 tile.
-// The swizzle only XORs chunk bits, so other k-steps / d-blocks are an XOR away:
-//   row operand (ds_read_b128) of k-step ks, rows 32 qb + l32:  (aoff ^ (ks << 5)) + qb * 32 * ROWB
-//   transposed operand (two ds_read_b64_tr_b16) of d-block db, rows 16 t + ...:
-//                         (troff[i] ^ (db << 6)) + t * 16 * ROWB, i = 0, 1
-template <int D>
-struct TileOffsets {
-  int aoff;
-  int troff[2];
-  __device__ __forceinline__ void init(int lane) {
-    constexpr int ROWB = D * 2;
-    const int hl = lane >> 5, l32 = lane & 31, g16 = lane & 15;
-    aoff = l32 * ROWB + ((hl ^ lds_swz<D>(l32)) << 4);
-    const int dcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
-    const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
-    const int r0 = 4 * hl + (g16 >> 2), r1 = r0 + 8;
-    troff[0] = r0 * ROWB + ((chunk ^ lds_swz<D>(r0)) * 16) + sub;
-    troff[1] = r1 * ROWB + ((chunk ^ lds_swz<D>(r1)) * 16) + sub;
-  }
-  __device__ __forceinline__ bf16x8 row_operand(const char FA_LDS* tile, int ks, int blk) const {
-    return lds_read16(tile + (aoff ^ (ks << 5)) + blk * 32 * D * 2);
-  }
-  __device__ __forceinline__ bf16x8 tr_operand(const char FA_LDS* tile, int t, int db) const {
-    return cat(lds_read_tr(tile + (troff[0] ^ (db << 6)) + t * 16 * D * 2),
-               lds_read_tr(tile + (troff[1] ^ (db << 6)) + t * 16 * D * 2));
-  }
-};
-
-// Stage a wave's 32 x D fp32 accumulator (transposed C layout: lane = row
-// l32, register r of block db = column db*32 + 8(r/4) + 4(l/32) + r%4) as bf16
-// through LDS and write whole 16-byte row segments to global memory.
-template <int D>
-__device__ __forceinline__ void store_rows_bf16(char FA_LDS* st, const f32x16* acc, float mul, __bf16* gbase,
-                                                long row_stride, int row0, int L, int lane) {
-  constexpr int OROWB = D * 2 + 16;
-  const int l32 = lane & 31, hl = lane >> 5;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dcol = db * 32 + 8 * g + 4 * hl;
-      const bf16x2 a = pack_bf16(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
-      const bf16x2 b = pack_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
-      *(bf16x4 FA_LDS*)(st + l32 * OROWB + dcol * 2) = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-    }
-  __builtin_amdgcn_wave_barrier();
-  constexpr int CPR = D / 8;
-  constexpr int PER_LANE = 32 * CPR / 64;
-#pragma unroll
-  for (int u = 0; u < PER_LANE; ++u) {
-    const int idx = u * 64 + lane;
-    const int row = idx / CPR, ch = idx % CPR;
-    const int r = row0 + row;
-    const bf16x8 v8 = *(const bf16x8 FA_LDS*)(st + row * OROWB + ch * 16);
-    if (r < L) *(bf16x8*)(gbase + (long)r * row_stride + ch * 8) = v8;
-  }
-}
-
-// Wait until at most `n` vector-memory operations of this wave are outstanding
-// (and no LDS operation); n is one of the few values the kernels use.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(5)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(9)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(10)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(16)); break;
-    case 18: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(18)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
-  }
 }
 
 }  // namespace
@@ -301,12 +177,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
     // LSE*log2(e) and D of the tile's rows: wave w moves rows (w & 1) * 32 + lane
     // of array w >> 1 (lanes 0..31)
     if (lane < 32) {
-      int r = q0 + (wave & 1) * 32 + lane;
-      r = r < L ? r : L - 1;
-      const long li = lse_index(p, s, h, seq0, r, T, VARLEN);
-      const float* src = (wave < 2 ? p.lse2 : p.dsum) + li;
-      __builtin_amdgcn_global_load_lds(src, stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128, 4, 0,
-                                       0);
+      // rows of one (sequence, head) are contiguous in the LSE layout
+      const int r0 = q0 + (wave & 1) * 32;
+      const int r = min(r0 + lane, L - 1);
+      const float* src = (wave < 2 ? p.lse2 : p.dsum) + lse_index(p, s, h, seq0, r0, T, VARLEN);
+      buf2lds4(buffer_rsrc(src), (unsigned)(r - r0) * 4u, stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128);
     }
     const char* qb = (const char*)p.q + ((long)seq0 * p.Hq + h) * D * 2;
     const char* ob = (const char*)p.dout + ((long)seq0 * p.Hq + h) * D * 2;

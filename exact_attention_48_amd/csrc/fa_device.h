@@ -53,6 +53,25 @@ __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// acc *= alpha for an accumulator held in AGPRs, in place (each register read
+// to a VGPR, multiplied, written back), so that the compiler never moves the
+// accumulator out of the AGPRs for VALU arithmetic. Callers wait for the
+// MFMAs that wrote `acc` first (mfma_result_wait).
+__device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
+  float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3], e4 = acc[4], e5 = acc[5], e6 = acc[6], e7 = acc[7];
+  float e8 = acc[8], e9 = acc[9], e10 = acc[10], e11 = acc[11], e12 = acc[12], e13 = acc[13], e14 = acc[14],
+        e15 = acc[15];
+  float t;
+#define FA_SCALE1(i) "v_accvgpr_read_b32 %16, %" #i "\n v_mul_f32 %16, %16, %17\n v_accvgpr_write_b32 %" #i ", %16\n"
+  asm volatile(FA_SCALE1(0) FA_SCALE1(1) FA_SCALE1(2) FA_SCALE1(3) FA_SCALE1(4) FA_SCALE1(5) FA_SCALE1(6)
+                   FA_SCALE1(7) FA_SCALE1(8) FA_SCALE1(9) FA_SCALE1(10) FA_SCALE1(11) FA_SCALE1(12) FA_SCALE1(13)
+                       FA_SCALE1(14) FA_SCALE1(15)
+               : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "+a"(e4), "+a"(e5), "+a"(e6), "+a"(e7), "+a"(e8),
+                 "+a"(e9), "+a"(e10), "+a"(e11), "+a"(e12), "+a"(e13), "+a"(e14), "+a"(e15), "=&v"(t)
+               : "v"(alpha));
+#undef FA_SCALE1
+  acc = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
+}
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory"); }
 // Keeps an asm MFMA result allocated up to this point (a result that is never
 // read would otherwise free its registers while the MFMA still writes them).
@@ -96,11 +115,22 @@ __device__ __forceinline__ bf16x8 lds_read16(const void FA_LDS* p) {
   return *(const bf16x8 FA_LDS*)p;
 }
 
-// One 16-byte global load per lane straight into LDS (global_load_lds_dwordx4).
-// The 64 lanes of the wave fill 1 KiB of LDS starting at `lds` (wave-uniform),
-// lane i at lds + 16 * i.
-__device__ __forceinline__ void g2lds16(const void* g, void FA_LDS* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+// HBM -> LDS loads without register staging use the buffer form
+// (buffer_load_dword{,x4} ... lds): the global (FLAT-encoded) form makes the
+// compiler treat every later LDS read as ordered behind it on the LDS counter,
+// so each wait for an operand would drain all reads in flight.
+// A buffer descriptor over `base` with no range limit in practice (callers
+// keep every offset inside the tensor themselves).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+// `bytes` (4 or 16) per lane from rsrc + voffset into LDS: the 64 lanes fill
+// 64 * bytes of LDS starting at `lds` (wave-uniform), lane i at lds + bytes * i.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, void FA_LDS* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, (int)voffset, 0, 0, 0);
+}
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, void FA_LDS* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 4, (int)voffset, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

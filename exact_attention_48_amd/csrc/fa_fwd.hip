@@ -1,137 +1,97 @@
 // fa_fwd.hip -- exact attention forward for gfx950 (MI355X).
 //
 // One workgroup computes BM = 256 query rows of one (sequence, query head)
-// with 8 waves of 32 rows each. The loop walks the key/value tiles of BN = 64
-// keys (tiling with an online softmax, so the N x N score matrix never leaves
-// the chip: "FlashAttention-4 Conquers Asymmetric GPU Hardware Scaling",
-// podcast.app episode page, second paragraph of the description).
+// with 4 waves, one per SIMD, each owning 64 queries as two 32-query MFMA
+// blocks. The loop walks the key/value tiles of BN = 32 keys (tiling with an
+// online softmax, so the N x N score matrix never leaves the chip:
+// "FlashAttention-4 Conquers Asymmetric GPU Hardware Scaling", podcast.app
+// episode page, second paragraph of the description).
 //
-// Per key/value tile j and wave:
-//   S^T[64 x 32] = K_j[64 x d] * Q_w^T[d x 32]     bf16 MFMA 32x32x16, fp32 acc
-//     -> every lane holds the scores of ONE query for 32 keys, so the row max
-//        is an in-lane max plus one v_permlane32_swap with the partner lane
+// Per key/value tile j and wave (query block qb = 0, 1):
+//   S^T[32 x 32] = K_j[32 x d] * Q_qb^T[d x 32]   bf16 MFMA 32x32x16, fp32 acc
+//     -> every lane holds the scores of ONE query for 16 of the tile's keys,
+//        so a row max is an in-lane max plus one v_permlane32_swap
 //   masking only on tiles that cross the causal diagonal or the sequence end
-//   conditional rescaling: the running max m (and with it O and the row sum l)
-//     only moves when a row's max grows by more than tau (log2 units);
-//     otherwise the stale m is kept, which is exact because O and l always
-//     share the same m (conditional online softmax rescaling: daily.dev
-//     "Summary"; FA4 abstract on the zhuanzhiai.com page)
+//   conditional rescaling: each row's max m stays at its first tile's max;
+//     a tile whose max exceeds m by more than tau (log2 units) only raises a
+//     flag, and a workgroup with a raised flag runs its loop a second time
+//     with the exact row maxima (the threshold-gated rescale of the pages,
+//     daily.dev "Summary" and the FA4 abstract on the zhuanzhiai.com page,
+//     moved out of the loop: O and l always share the same m, so no pass
+//     ever rescales O)
 //   P = exp2(S c - m c), c = scale * log2(e), hardware v_exp_f32 or the
 //     FMA-pipe polynomial (software exponential: daily.dev "Summary")
 //   l += rowsum(P) (per-lane partial sums, combined once at the end)
-//   O^T[d x 32] += V^T[d x 64] * P^T[64 x 32]      bf16 MFMA; P stays in
+//   O^T[d x 32] += V_j^T[d x 32] * P^T[32 x 32]  bf16 MFMA; P stays in
 //     registers as the B operand; V^T comes from row-major V in LDS through
 //     the transposing ds_read_b64_tr_b16
+// Every K and V^T fragment read from LDS feeds both query blocks, which
+// halves the LDS traffic per MFMA against one block per wave. Q fragments
+// and the O accumulators sit in the accumulation registers.
 //
-// Ping-pong (the MMA/softmax overlap of the pages' pipeline, daily.dev
-// "Summary"): the 8 waves form two groups of 4, one wave of each group on
-// every SIMD. Time is cut into phases by workgroup barriers; in a phase one
-// group runs an MFMA phase (O += V_{j-1} P_{j-1}, then S_j = K_j Q^T) while
-// the other runs the VALU phase of its previous tile (mask, max, rescale,
-// exp2, row sums, bf16 pack). The groups are one phase apart, so every SIMD
-// always has one wave feeding the matrix core and one feeding the VALU.
+// Software pipeline (the MMA/softmax overlap of the pages' pipeline, daily.dev
+// "Summary"), iteration j of a wave, one MFMA stream:
+//   phase A : S of tile j+1 (16 MFMAs), interleaved with the exps of tile j
+//             for query block 0 and half of block 1;
+//   phase B1: O_0 += V_j P_0 (8 MFMAs), with the other exps of block 1;
+//   phase B2: O_1 += V_j P_1 (8 MFMAs), with the masking, row maxima and
+//             threshold checks of tile j+1 (its S is done by then).
 //
-// K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging) into two-deep rings of distinct LDS objects; a copy issued in one
-// phase is waited for at the end of the next, and the phase barriers carry
-// no memory fence (that would drain the copies still in flight).
+// K and V tiles travel HBM -> LDS with buffer_load ... lds (no register
+// staging) through a 4-deep ring of distinct LDS objects, issued two
+// iterations ahead; one workgroup barrier per iteration, without the memory
+// fence of __syncthreads (that would drain the copies still in flight). The
+// buffer form (rather than the flat global_load_lds) lets the compiler count
+// outstanding LDS reads separately from the copies, so a fragment read waits
+// only for itself.
 //
 // Work order: query tiles are ordered heaviest first (causal: the last tiles
 // of a sequence see the most keys) -- longest-processing-time-first (daily.dev
 // "Summary") -- and the G query heads of one K/V head are kept on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin) so they share its L2.
-#include <type_traits>
-
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tiles.h"
 
 namespace fa {
 
+using namespace tiles;
+
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 64;
-constexpr int NWAVES = 8;
-constexpr int NTHREADS = 64 * NWAVES;
+constexpr int WQ = 64;               // queries per wave
+constexpr int BM = NWAVES * WQ;      // queries per workgroup
+constexpr int BN = 32;               // keys per K/V tile
 
 template <int D>
-struct Geo {
-  static constexpr int ROWB = D * 2;              // bytes per K/V row
-  static constexpr int TILEB = BN * ROWB;         // bytes per K or V tile
-  static constexpr int KSTEPS = D / 16;           // MFMA k-steps of S = K Q^T
-  static constexpr int DBLK = D / 32;             // 32-row blocks of O^T
-  static_assert(2 * 32 * ROWB <= TILEB, "two waves' O staging must fit in one tile buffer");
-};
-
-// HBM -> LDS copy of one K or V tile (BN rows x D, rows clamped to L-1 on the
-// tail tile; those columns are masked). Each wave of group 0 moves PER_WAVE KiB.
-template <int D>
-struct TileCopy {
-  static constexpr int LPR = Geo<D>::ROWB / 16;   // lanes per row
-  static constexpr int RPI = 64 / LPR;            // rows per wave instruction (1 KiB)
-  static constexpr int NI = BN / RPI;             // instructions per tile
-  static constexpr int COPY_WAVES = NWAVES / 2;   // the waves of ping-pong group 0 move the tiles
-  static constexpr int PER_WAVE = NI / COPY_WAVES;
-  static_assert(PER_WAVE * COPY_WAVES == NI, "tile copy must split evenly over the waves");
-  unsigned off[PER_WAVE];                         // row * stride + swizzled chunk * 16
-  int wave, lane;
-
-  __device__ __forceinline__ int row(int u) const { return (wave * PER_WAVE + u) * RPI + lane / LPR; }
-  __device__ __forceinline__ unsigned chunk16(int u) const {
-    return (unsigned)(((lane % LPR) ^ lds_swz<D>(row(u))) * 16);
-  }
-  __device__ __forceinline__ void init(int wave_, int lane_, unsigned stride) {
-    wave = wave_;
-    lane = lane_;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) off[u] = (unsigned)row(u) * stride + chunk16(u);
-  }
-  // `base` points at row 0 of this head's K (or V); kt is the tile index.
-  __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int kt, int L) const {
-    const char* tb = base + (long)kt * BN * stride;
-    char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
-    if (kt * BN + BN <= L) {
-#pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        // keep the 64-bit address out of loop-invariant code motion: uniform
-        // base + 32-bit lane offset is the SGPR-base addressing form
-        unsigned o = off[u];
-        asm volatile("" : "+v"(o));
-        g2lds16(tb + o, dst + u * 1024);
-      }
-    } else {
-      const int last = L - 1 - kt * BN;
-#pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        const int r = min(row(u), last);
-        g2lds16(tb + ((unsigned)r * (unsigned)stride + chunk16(u)), dst + u * 1024);
-      }
-    }
-  }
+struct FwdStage {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BN * ROWB;           // one K or V tile
+  static constexpr int BYTES = 2 * TILEB;
+  static constexpr int OROWB = ROWB + 16;           // output staging pitch
+  static_assert(32 * OROWB <= BYTES, "32 rows of a wave's output staging must fit in one stage");
 };
 
 }  // namespace
 
 template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(const FwdParams p) {
-  using G = Geo<D>;
-  constexpr int KSTEPS = G::KSTEPS;
-  constexpr int DBLK = G::DBLK;
-  constexpr int ROWB = G::ROWB;
-  __shared__ __attribute__((aligned(1024))) char k0_raw[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k1_raw[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v0_raw[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v1_raw[G::TILEB];
-  char FA_LDS* const kbuf[2] = {(char FA_LDS*)k0_raw, (char FA_LDS*)k1_raw};
-  char FA_LDS* const vbuf[2] = {(char FA_LDS*)v0_raw, (char FA_LDS*)v1_raw};
+  using S = FwdStage<D>;
+  using RC = RowCopy<D, BN>;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int OPS = 2 * RC::PER_WAVE;             // copy instructions per tile and wave
+  __shared__ __attribute__((aligned(1024))) char s0_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s1_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s2_raw[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char s3_raw[S::BYTES];
+  char FA_LDS* const stg[NSTAGE] = {(char FA_LDS*)s0_raw, (char FA_LDS*)s1_raw, (char FA_LDS*)s2_raw,
+                                    (char FA_LDS*)s3_raw};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave >> 2;           // ping-pong group: waves 0-3 / 4-7 (one of each per SIMD)
-  const int hl = lane >> 5;            // which half of the wave (0/1)
-  const int l32 = lane & 31;
-  const int g16 = lane & 15;
+  const int hl = lane >> 5, l32 = lane & 31;
 
   // ---- work item -> (sequence, head, query tile) ----
   int w = blockIdx.x;
@@ -159,241 +119,296 @@ void fa_fwd_kernel(const FwdParams p) {
   }
   const int q0 = qt * BM;
   if (q0 >= L) return;
-  const int qw0 = q0 + wave * 32;                     // first row of this wave
-  const int my_q = qw0 + l32;                         // this lane's query (local position)
+  const int qw0 = q0 + wave * WQ;                   // first query of this wave
+  int my_q[2];
+  my_q[0] = qw0 + l32;
+  my_q[1] = qw0 + 32 + l32;
 
-  const long q_row_stride = (long)p.Hq * D;           // elements
-  const long kv_stride = (long)p.Hkv * D * 2;         // bytes per token row of K/V
+  const long q_row_stride = (long)p.Hq * D;         // elements
+  const long kv_stride = (long)p.Hkv * D * 2;       // bytes per token row of K/V
   const char* kbase = (const char*)p.k + ((long)seq0 * p.Hkv + hkv) * D * 2;
   const char* vbase = (const char*)p.v + ((long)seq0 * p.Hkv + hkv) * D * 2;
+  const int kv_end = CAUSAL ? min(L, q0 + BM) : L;  // keys this workgroup can see
+  const int n_it = (kv_end + BN - 1) / BN;
 
-  const int kv_end = CAUSAL ? min(L, q0 + BM) : L;    // keys this workgroup can see
-  const int n_kv = (kv_end + BN - 1) / BN;
-  // tiles this wave computes (causal: stop after the tile holding its last row)
-  const int n_w = CAUSAL ? min(n_kv, (qw0 + 31) / BN + 1) : n_kv;
-
-  TileCopy<D> copy;
-  copy.init(wave & 3, lane, (unsigned)kv_stride);
-  if (grp == 0) copy.issue(kbuf[0], kbase, kv_stride, 0, L);
-
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query my_q ----
-  bf16x8 qf[KSTEPS];
-  {
-    const __bf16* qp = (const __bf16*)p.q + ((long)(seq0 + my_q) * p.Hq + h) * D + hl * 8;
+  // ---- Q fragments (B operands of S^T = K Q^T): lane holds queries my_q[qb] ----
+  bf16x8 qf[2][KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      if (my_q < L) qf[ks] = *(const bf16x8*)(qp + ks * 16);
-      else qf[ks] = bf16x8{};
-    }
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qr = my_q[qb] < L ? my_q[qb] : L - 1;
+    const __bf16* qp = (const __bf16*)p.q + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
   }
 
-  // Loop-invariant per-lane LDS read offsets. The swizzle only XORs chunk
-  // bits, so the offsets of other k-steps / d-blocks are these XOR a constant:
-  //   K fragment of k-step ks (A operand of S^T): koff ^ (ks << 5), +32 rows for key block 1
-  //   V^T fragment of d-block db (keys +0..3 / +8..11): voff[i] ^ (db << 6), +16 rows per key step t
-  const int koff = l32 * ROWB + ((hl ^ lds_swz<D>(l32)) << 4);
-  int voff[2];
-  {
-    const int dcol = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
-    const int chunk = dcol >> 3, sub = (dcol & 7) * 2;
-    const int r0 = 4 * hl + (g16 >> 2), r1 = r0 + 8;
-    voff[0] = r0 * ROWB + ((chunk ^ lds_swz<D>(r0)) * 16) + sub;
-    voff[1] = r1 * ROWB + ((chunk ^ lds_swz<D>(r1)) * 16) + sub;
-  }
+  RC copy;
+  copy.init(wave, lane, (unsigned)kv_stride);
+  int iss = 0;
+  auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
+    copy.issue(stage, kbase, kv_stride, iss * BN, L);
+    copy.issue(stage + S::TILEB, vbase, kv_stride, iss * BN, L);
+    ++iss;
+  };
 
+  TileOffsets<D> to;
+  to.init(lane);
   const float c = p.scale_log2;
   const float tau = p.tau;
-  f32x16 oacc[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;     // running max of raw scores (stale by at most tau / c)
-  float l_run = 0.f;           // partial row sum over this lane's keys
-  f32x16 sacc[2];              // S^T of the tile between its MFMA phase and its VALU phase
-  bf16x8 pb[4];                // P of the tile between its VALU phase and the next MFMA phase
+  f32x16 oacc[2][DBLK];
+  float m_run[2];                            // the max O and l are relative to (fixed in a pass)
+  float mc[2];                               // m_run * c (0 for a row without a visible key yet)
+  float l_run[2];                            // partial row sums over this lane's keys
+  float m_seen[2];                           // true running max of the scores
+  bool over[2];                              // some tile's max exceeded m_run by more than tau
+  f32x16 sA[2], sB[2];                       // S^T of two consecutive tiles, per query block
+  u32x4 pb[2][2];                            // P^T (bf16 pairs) of the current tile [qb][key step]
 
-  // MFMA phase m: O += V_{m-1} P_{m-1} (if the wave computed tile m-1), then
-  // S_m = K_m Q^T (if the wave computes tile m).
-  auto mfma_phase = [&](const char FA_LDS* kb, const char FA_LDS* vb, int m) __attribute__((always_inline)) {
-    // One stream of MFMA steps: NPV steps of O += V^T P^T (t = i / DBLK,
-    // db = i % DBLK), then NQK steps of S^T = K Q^T (ks = j / 2, key block
-    // j % 2). A operands are read PF steps ahead through a small register
-    // queue; a scheduling fence after each step keeps the compiler from
-    // hoisting every read of the phase (register pressure).
-    constexpr int NPV = 4 * DBLK, NQK = 2 * KSTEPS, PF = 4;
-    const bool do_pv = m >= 1 && m - 1 < n_w;
-    const bool do_qk = m < n_w;
-    const int first = do_pv ? 0 : NPV;
-    const int last = do_qk ? NPV + NQK : NPV;
-    auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-      if (i < NPV) {
-        const int t = i / DBLK, db = i % DBLK;
-        return cat(lds_read_tr(vb + (voff[0] ^ (db << 6)) + t * 16 * ROWB),
-                   lds_read_tr(vb + (voff[1] ^ (db << 6)) + t * 16 * ROWB));
-      }
-      const int j = i - NPV;
-      return lds_read16(kb + (koff ^ ((j >> 1) << 5)) + (j & 1) * 32 * ROWB);
-    };
-    auto step = [&](int i, const bf16x8& a) __attribute__((always_inline)) {
-      if (i < NPV) {
-        oacc[i % DBLK] = mfma32(a, pb[i / DBLK], oacc[i % DBLK]);
-      } else {
-        const int j = i - NPV;
-        sacc[j & 1] = mfma32(a, qf[j >> 1], sacc[j & 1]);
-      }
-    };
-    (void)first;
-    (void)last;
-    if (do_pv) {
-      bf16x8 q[PF];
+  // S^T MFMA j: k-step j / 2, query block j % 2; the K fragment of a k-step is
+  // read once for both blocks.
+  constexpr int NA = 2 * KSTEPS;
+  auto a_frag = [&](const char FA_LDS* tile, int ks) __attribute__((always_inline)) {
+    return to.row_operand(tile, ks, 0);
+  };
+  auto a_step = [&](f32x16 (&sx)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
+    const int ks = j >> 1, qb = j & 1;
+    if (ks == 0) mfma_v_first(sx[qb], a, qf[qb][ks]);
+    else mfma_v(sx[qb], a, qf[qb][ks]);
+  };
+  // V^T fragment f: key step t = f / DBLK, d-block db = f % DBLK (both query blocks)
+  constexpr int NV = 2 * DBLK;
+  auto v_frag = [&](const char FA_LDS* tile, int f) __attribute__((always_inline)) {
+    return to.tr_operand(tile + S::TILEB, f / DBLK, f % DBLK);
+  };
+
+  // ---- softmax pieces ----
+  // exp element (qb, r) of the current tile (S^T in sc): key 8(r/4) + 4 hl + r%4
+  // of the tile, query my_q[qb]
+  // The 32 exp elements of a tile, u = 16 qb + r, run as a three-stage
+  // software pipeline so that no instruction of a slot waits on another one
+  // of the same slot: step t does x_t = S c - m c, p_{t-1} = exp2(x_{t-1}),
+  // and l += p_{t-2} (packing the bf16 pair when t-2 is odd).
+  float xq[3], pq[3];
+  auto exp_step = [&](const f32x16 (&sc)[2], int t) __attribute__((always_inline)) {
+    if (t < 32) {
+      const int qb = t >> 4, r = t & 15;
+      xq[t % 3] = __builtin_fmaf(sc[qb][r], c, -mc[qb]);
+    }
+    if (t >= 1 && t <= 32) pq[(t - 1) % 3] = exp2_sel<EXPMODE>(xq[(t - 1) % 3]);
+    if (t >= 2 && t <= 33) {
+      const int u = t - 2, qb = u >> 4, r = u & 15;
+      l_run[qb] += pq[u % 3];
+      if (r & 1) pb[qb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(pq[(u - 1) % 3], pq[u % 3]));
+    }
+  };
+  // Masking of a tile (keys k0..): dead scores -> -inf.
+  auto mask_tile = [&](f32x16 (&sx)[2], int k0) __attribute__((always_inline)) {
+    asm volatile("; masking");   // keeps the caller's branch a branch (no if-conversion)
 #pragma unroll
-      for (int i = 0; i < PF; ++i) q[i] = fetch(i);
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        const bf16x8 a = q[i % PF];
-        if (i + PF < NPV) q[i % PF] = fetch(i + PF);
-        step(i, a);
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool dead = (key >= L) || (CAUSAL && key > my_q[qb]);
+        if (dead) sx[qb][r] = -INFINITY;
+      }
+  };
+  auto needs_mask = [&](int k0) __attribute__((always_inline)) {
+    return (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > qw0);
+  };
+  float mpart[2];
+  auto max_half = [&](const f32x16 (&sx)[2], int qb, int half) __attribute__((always_inline)) {
+    float m = fmaxf(sx[qb][8 * half], sx[qb][8 * half + 1]);
+#pragma unroll
+    for (int r = 8 * half + 2; r < 8 * half + 8; r += 2) m = fmaxf(m, fmaxf(sx[qb][r], sx[qb][r + 1]));
+    if (half == 0) mpart[qb] = m;
+    else mpart[qb] = fmaxf(mpart[qb], m);
+  };
+  auto decide = [&](int qb) __attribute__((always_inline)) {
+    const float mx = pair_max(mpart[qb]);
+    m_seen[qb] = fmaxf(m_seen[qb], mx);
+    over[qb] = over[qb] || ((mx - m_run[qb]) * c > tau);   // false when both are -inf
+  };
+  // ---- one iteration's MFMA stream ----
+  // Softmax work of the current tile (S^T in sc), spread over the MFMA slots:
+  //   phase A : exp pipeline steps 0..UA-1 (query block 0 and half of block 1)
+  //   phase B1: exp pipeline steps UA..33 (the rest of block 1; P of block 0
+  //             is complete after step 17, so phase B1 can start)
+  //   phase B2: masking / maxima / decisions of the next tile (S^T in sx)
+  constexpr int UA = 24;
+  constexpr int UB = 34 - UA;
+  constexpr int VPRE = (PF < NV) ? PF : NV;         // V^T fragments read during phase A
+  auto stream = [&](const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2], const f32x16 (&sc)[2],
+                    int k_next, bool issue, char FA_LDS* issue_stage) __attribute__((always_inline)) {
+    bf16x8 qa[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) qa[i] = a_frag(nt, i);
+    if (issue) issue_next(issue_stage);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 vf[NV];                                  // V^T fragments, kept for both query blocks
+    // phase A: S^T of the next tile; fragment ks feeds MFMAs 2 ks and 2 ks + 1
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bf16x8 a = qa[ks % PF];
+      if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(nt, ks + PF);
+      else if (ks + PF - KSTEPS < VPRE) vf[ks + PF - KSTEPS] = v_frag(ct, ks + PF - KSTEPS);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = 2 * ks + x;
+        a_step(sx, j, a);
+#pragma unroll
+        for (int t = UA * j / NA; t < UA * (j + 1) / NA; ++t) exp_step(sc, t);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (do_qk) {
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-      bf16x8 q[PF];
+    // phase B1: O_0 += V^T P_0, with the remaining exps of block 1
+    asm volatile("s_nop 2");                        // VALU-written B operands -> MFMA
 #pragma unroll
-      for (int i = 0; i < PF; ++i) q[i] = fetch(NPV + i);
+    for (int f = 0; f < NV; ++f) {
+      if (f + VPRE < NV) vf[f + VPRE] = v_frag(ct, f + VPRE);
+      mfma_a(oacc[0][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[0][f / DBLK]));
 #pragma unroll
-      for (int i = NPV; i < NPV + NQK; ++i) {
-        const bf16x8 a = q[(i - NPV) % PF];
-        if (i + PF < NPV + NQK) q[(i - NPV) % PF] = fetch(i + PF);
-        step(i, a);
+      for (int t = UA + UB * f / NV; t < UA + UB * (f + 1) / NV; ++t) exp_step(sc, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase B2: O_1 += V^T P_1, with the next tile's masking, maxima, decisions
+    asm volatile("s_nop 2");
+    const bool mask_next = needs_mask(k_next);
+#pragma unroll
+    for (int f = 0; f < NV; ++f) {
+      mfma_a(oacc[1][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[1][f / DBLK]));
+      // work item w of the 6: mask+max(0, lo), max(0, hi), decide(0), max(1, lo), max(1, hi), decide(1)
+#pragma unroll
+      for (int wi = 6 * f / NV; wi < 6 * (f + 1) / NV; ++wi) {
+        if (wi == 0) {
+          if (mask_next) mask_tile(sx, k_next);
+          max_half(sx, 0, 0);
+        }
+        if (wi == 1) max_half(sx, 0, 1);
+        if (wi == 2) decide(0);
+        if (wi == 3) max_half(sx, 1, 0);
+        if (wi == 4) max_half(sx, 1, 1);
+        if (wi == 5) decide(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Iteration i (BI = i % NSTAGE): tile i in stg[BI] (its S^T in the array of
+  // parity i), tile i+1 in stg[BI+1]; tile i+3 is copied into stg[BI+3] (last
+  // read as tile i-1, before this iteration's barrier). The S^T MFMAs of tile
+  // i+1 also run on the last iteration (stale LDS, results unused).
+  auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
+    constexpr int BI = decltype(bi_tag)::value;
+    if (i + 2 < n_it) wait_vm(OPS);
+    else if (i + 1 < n_it) wait_vm(0);
+    barrier_no_fence();
+    const bool issue = i + 3 < n_it;
+    char FA_LDS* const nst = stg[(BI + 3) % NSTAGE];
+    const int k_next = (i + 1) * BN;
+    if constexpr (BI % 2 == 0) stream(stg[(BI + 1) % NSTAGE], stg[BI], sB, sA, k_next, issue, nst);
+    else stream(stg[(BI + 1) % NSTAGE], stg[BI], sA, sB, k_next, issue, nst);
+  };
+
+  // Rescaling, taken out of the loop: in the first pass each row's max is
+  // fixed at its first tile's max, and every later tile only records its true
+  // max and whether it exceeded the fixed one by more than tau (log2 units).
+  // If none did (the common case) O and l share that max, every P is at most
+  // 2^tau, and the pass is exact. Otherwise the workgroup runs the loop again
+  // with each row's true maximum, where no rescaling can be needed.
+  __shared__ int over_flag[NWAVES];
+  for (int pass = 0;; ++pass) {
+    iss = 0;
+    issue_next(stg[0]);
+    if (n_it > 1) issue_next(stg[1]);
+    if (n_it > 2) issue_next(stg[2]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
+      l_run[qb] = 0.f;
+      m_run[qb] = pass == 0 ? -INFINITY : m_seen[qb];
+      m_seen[qb] = -INFINITY;
+      over[qb] = false;
+    }
+
+    // ---- prologue: tile 0 in, S^T of tile 0 and its maxima ----
+    if (n_it > 2) wait_vm(2 * OPS);
+    else if (n_it > 1) wait_vm(OPS);
+    else wait_vm(0);
+    barrier_no_fence();
+    {
+      bf16x8 qa[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) qa[i] = a_frag(stg[0], i);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 a = qa[ks % PF];
+        if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(stg[0], ks + PF);
+        a_step(sA, 2 * ks, a);
+        a_step(sA, 2 * ks + 1, a);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  };
+    mfma_result_wait();
+    if (needs_mask(0)) mask_tile(sA, 0);
+    max_half(sA, 0, 0);
+    max_half(sA, 0, 1);
+    max_half(sA, 1, 0);
+    max_half(sA, 1, 1);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mx = pair_max(mpart[qb]);
+      m_seen[qb] = mx;
+      if (pass == 0) m_run[qb] = mx;
+      mc[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb] * c;
+    }
 
-  // VALU phase of tile m: mask, row max, conditional rescale, P = exp2(S c - m c).
-  auto valu_phase = [&](int m) __attribute__((always_inline)) {
-    if (m >= n_w) return;
-    const int k0 = m * BN;
-    if ((k0 + BN > L) || (CAUSAL && (k0 + BN - 1 > qw0))) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool dead = (key >= L) || (CAUSAL && key > my_q);
-          if (dead) sacc[kb][r] = -INFINITY;
-        }
+    for (int i = 0; i < n_it; i += NSTAGE) {
+      iter(ic<0>{}, i);
+      if (i + 1 < n_it) iter(ic<1>{}, i + 1);
+      if (i + 2 < n_it) iter(ic<2>{}, i + 2);
+      if (i + 3 < n_it) iter(ic<3>{}, i + 3);
     }
-    float ma = fmaxf(sacc[0][0], sacc[0][1]), mb = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      ma = fmaxf(ma, fmaxf(sacc[0][r], sacc[0][r + 1]));
-      mb = fmaxf(mb, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    for (int x = 0; x < 2; ++x) {
+      keep_live(sA[x]);
+      keep_live(sB[x]);
     }
-    const float mx = pair_max(fmaxf(ma, mb));
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = (m_new - m_run) * c > tau;   // false when both are -inf
-    if (wave_any(grow)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_sel<0>((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-    float lsum[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = exp2_sel<EXPMODE>(__builtin_fmaf(sacc[kb][8 * half + e], c, -mc));
-        lsum[kb * 2 + half] = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        bf16x8 b;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 t = pack_bf16(pv[e], pv[e + 1]);
-          b[e] = t[0];
-          b[e + 1] = t[1];
-        }
-        pb[kb * 2 + half] = b;
-      }
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-  };
-
-  wait_vmem();
-  __syncthreads();
-
-  // Both groups run the same sequence of phases; group 1 starts one barrier
-  // later (and group 0 ends with one extra barrier), so when group 0 is in its
-  // MFMA phase m, group 1 is in its VALU phase m-1, and the other way round.
-  // Iteration m of a wave (PAR = m & 1 selects the ring slots):
-  //   group 0 copies K_{m+1} -> kbuf[1-PAR] and V_m -> vbuf[PAR];
-  //   MFMA phase m (K_m in kbuf[PAR], V_{m-1} in vbuf[1-PAR]); barrier;
-  //   VALU phase m; group 0 waits for its copies; barrier.
-  // A slot is overwritten only after its previous tile's last reader (group 1,
-  // one phase behind) has passed the barrier that ends that read.
-  auto iter = [&](auto par_tag, const int m) __attribute__((always_inline)) {
-    constexpr int PAR = decltype(par_tag)::value;
-    if (grp == 0) {
-      if (m + 1 < n_kv) copy.issue(kbuf[1 - PAR], kbase, kv_stride, m + 1, L);
-      if (m < n_kv) copy.issue(vbuf[PAR], vbase, kv_stride, m, L);
-    }
-    mfma_phase(kbuf[PAR], vbuf[1 - PAR], m);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-    barrier_no_fence();
-    valu_phase(m);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    barrier_no_fence();
-  };
-  if (grp == 1) barrier_no_fence();
-  for (int m = 0; m <= n_kv; m += 2) {
-    iter(std::integral_constant<int, 0>{}, m);
-    if (m + 1 <= n_kv) iter(std::integral_constant<int, 1>{}, m + 1);
+    mfma_result_wait();
+    if (pass == 1) break;
+    // all copies have landed (the last iterations wait for them); LDS is free
+    // once every wave is past this point
+    const bool any = wave_any(over[0] || over[1]);
+    if (lane == 0) over_flag[wave] = any ? 1 : 0;
+    __syncthreads();
+    const bool again = over_flag[0] | over_flag[1] | over_flag[2] | over_flag[3];
+    __syncthreads();
+    if (!again) break;
   }
-  if (grp == 0) barrier_no_fence();
 
   // ---- epilogue: O = O / l, LSE = m * scale + ln(l) ----
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // Stage O (bf16) through LDS so global stores are whole 16-byte row
-  // segments; row r's chunk ch sits at chunk (ch ^ r) mod (D / 8).
-  constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  char FA_LDS* ost = (wave < 2 ? kbuf[0] : wave < 4 ? kbuf[1] : wave < 6 ? vbuf[0] : vbuf[1]) +
-                     (wave & 1) * 32 * ROWB;
+  barrier_no_fence();
+  char FA_LDS* st = stg[0];
+  if (wave == 1) st = stg[1];
+  if (wave == 2) st = stg[2];
+  if (wave == 3) st = stg[3];
+  __bf16* obase = (__bf16*)p.o + ((long)seq0 * p.Hq + h) * D;
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int ch = db * 4 + g;               // chunk holding d = 8 ch .. 8 ch + 7
-      const bf16x2 a = pack_bf16(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-      const bf16x2 b = pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-      *(bf16x4 FA_LDS*)(ost + l32 * ROWB + ((ch ^ l32) & (CPR - 1)) * 16 + hl * 8) =
-          __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l_tot = pair_sum(l_run[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qb == 1) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
     }
-  __builtin_amdgcn_wave_barrier();
-  {
-    constexpr int PER_LANE = 32 * CPR / 64;
-    __bf16* obase = (__bf16*)p.o + ((long)seq0 * p.Hq + h) * D;
-#pragma unroll
-    for (int u = 0; u < PER_LANE; ++u) {
-      const int idx = u * 64 + lane;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int q = qw0 + row;
-      const bf16x8 v8 = *(const bf16x8 FA_LDS*)(ost + row * ROWB + ((ch ^ row) & (CPR - 1)) * 16);
-      if (q < L) *(bf16x8*)(obase + (long)q * q_row_stride + ch * 8) = v8;
+    store_rows_bf16<D>(st, oacc[qb], inv, obase, q_row_stride, qw0 + 32 * qb, L, lane);
+    if (hl == 0 && my_q[qb] < L) {
+      const float lse = (m_run[qb] == -INFINITY) ? -INFINITY : (m_run[qb] * c + __log2f(l_tot)) * kLn2;
+      long li;
+      if constexpr (VARLEN) li = (long)h * p.cu_seqlens[p.B] + seq0 + my_q[qb];
+      else li = ((long)s * p.Hq + h) * p.N + my_q[qb];
+      p.lse[li] = lse;
     }
-  }
-  if (hl == 0 && my_q < L) {
-    const float lse = (m_run == -INFINITY) ? -INFINITY : (m_run * c + __log2f(l_tot)) * kLn2;
-    long li;
-    if constexpr (VARLEN) li = (long)h * p.cu_seqlens[p.B] + seq0 + my_q;
-    else li = ((long)s * p.Hq + h) * p.N + my_q;
-    p.lse[li] = lse;
   }
 }
 
