@@ -187,15 +187,20 @@ def main():
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
         def time_it(fn, reps):
-            fn()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
+            # three warm calls, then the median of three timed windows
+            for _ in range(3):
                 fn()
-            b.record(stream)
             torch.cuda.synchronize()
-            return a.elapsed_time(b) / reps
+            windows = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                windows.append(a.elapsed_time(b) / reps)
+            return sorted(windows)[1]
 
         for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
                      "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64"):

@@ -78,9 +78,23 @@ __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n s_n
 __device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
 
 // Both lanes of the pair (l, l ^ 32) receive max(x[l], x[l ^ 32]).
+// Maxima as plain v_max / v_max3. fmaxf on values produced by inline asm
+// costs an extra canonicalising v_max per operand; scores are never
+// signalling NaNs, so the plain instructions give the same result.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Both lanes of the pair (l, l ^ 32) receive x[l] + x[l ^ 32].
@@ -138,6 +152,10 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // s_waitcnt immediate: at most `vm` vector-memory operations (which include the
 // HBM->LDS copies) and no LDS operation of this wave outstanding.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
+// vmcnt <= vm and lgkmcnt <= lgkm (lgkm <= 15; 15 does not wait on LDS at all)
+constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
 
 // Workgroup barrier WITHOUT the memory fence of __syncthreads(): that fence
 // waits for every outstanding vector-memory operation, i.e. it would drain the

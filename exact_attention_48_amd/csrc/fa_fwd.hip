@@ -86,8 +86,16 @@ void fa_fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char s1_raw[S::BYTES];
   __shared__ __attribute__((aligned(1024))) char s2_raw[S::BYTES];
   __shared__ __attribute__((aligned(1024))) char s3_raw[S::BYTES];
-  char FA_LDS* const stg[NSTAGE] = {(char FA_LDS*)s0_raw, (char FA_LDS*)s1_raw, (char FA_LDS*)s2_raw,
-                                    (char FA_LDS*)s3_raw};
+  // stage j (a compile-time constant wherever it is used; an array of LDS
+  // pointers can end up in global memory, which the linker cannot resolve)
+  auto stage = [&](int j) __attribute__((always_inline)) -> char FA_LDS* {
+    switch (j) {
+      case 0: return (char FA_LDS*)s0_raw;
+      case 1: return (char FA_LDS*)s1_raw;
+      case 2: return (char FA_LDS*)s2_raw;
+      default: return (char FA_LDS*)s3_raw;
+    }
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -197,6 +205,7 @@ void fa_fwd_kernel(const FwdParams p) {
     if (t >= 2 && t <= 33) {
       const int u = t - 2, qb = u >> 4, r = u & 15;
       l_run[qb] += pq[u % 3];
+      asm volatile("" : "+v"(l_run[qb]));   // keep the add in its slot (not sunk past the mask branch)
       if (r & 1) pb[qb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(pq[(u - 1) % 3], pq[u % 3]));
     }
   };
@@ -217,15 +226,16 @@ void fa_fwd_kernel(const FwdParams p) {
   };
   float mpart[2];
   auto max_half = [&](const f32x16 (&sx)[2], int qb, int half) __attribute__((always_inline)) {
-    float m = fmaxf(sx[qb][8 * half], sx[qb][8 * half + 1]);
-#pragma unroll
-    for (int r = 8 * half + 2; r < 8 * half + 8; r += 2) m = fmaxf(m, fmaxf(sx[qb][r], sx[qb][r + 1]));
-    if (half == 0) mpart[qb] = m;
-    else mpart[qb] = fmaxf(mpart[qb], m);
+    const int r = 8 * half;
+    const float a = vmax3(sx[qb][r], sx[qb][r + 1], sx[qb][r + 2]);
+    const float b = vmax3(sx[qb][r + 3], sx[qb][r + 4], sx[qb][r + 5]);
+    const float m = vmax3(a, b, sx[qb][r + 6]);
+    if (half == 0) mpart[qb] = vmax(m, sx[qb][r + 7]);
+    else mpart[qb] = vmax3(mpart[qb], m, sx[qb][r + 7]);
   };
   auto decide = [&](int qb) __attribute__((always_inline)) {
     const float mx = pair_max(mpart[qb]);
-    m_seen[qb] = fmaxf(m_seen[qb], mx);
+    m_seen[qb] = vmax(m_seen[qb], mx);
     over[qb] = over[qb] || ((mx - m_run[qb]) * c > tau);   // false when both are -inf
   };
   // ---- one iteration's MFMA stream ----
@@ -293,8 +303,8 @@ void fa_fwd_kernel(const FwdParams p) {
     }
   };
 
-  // Iteration i (BI = i % NSTAGE): tile i in stg[BI] (its S^T in the array of
-  // parity i), tile i+1 in stg[BI+1]; tile i+3 is copied into stg[BI+3] (last
+  // Iteration i (BI = i % NSTAGE): tile i in stage BI (its S^T in the array of
+  // parity i), tile i+1 in stage BI+1; tile i+3 is copied into stage BI+3 (last
   // read as tile i-1, before this iteration's barrier). The S^T MFMAs of tile
   // i+1 also run on the last iteration (stale LDS, results unused).
   auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
@@ -303,10 +313,10 @@ void fa_fwd_kernel(const FwdParams p) {
     else if (i + 1 < n_it) wait_vm(0);
     barrier_no_fence();
     const bool issue = i + 3 < n_it;
-    char FA_LDS* const nst = stg[(BI + 3) % NSTAGE];
+    char FA_LDS* const nst = stage((BI + 3) % NSTAGE);
     const int k_next = (i + 1) * BN;
-    if constexpr (BI % 2 == 0) stream(stg[(BI + 1) % NSTAGE], stg[BI], sB, sA, k_next, issue, nst);
-    else stream(stg[(BI + 1) % NSTAGE], stg[BI], sA, sB, k_next, issue, nst);
+    if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, k_next, issue, nst);
+    else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, k_next, issue, nst);
   };
 
   // Rescaling, taken out of the loop: in the first pass each row's max is
@@ -318,9 +328,9 @@ void fa_fwd_kernel(const FwdParams p) {
   __shared__ int over_flag[NWAVES];
   for (int pass = 0;; ++pass) {
     iss = 0;
-    issue_next(stg[0]);
-    if (n_it > 1) issue_next(stg[1]);
-    if (n_it > 2) issue_next(stg[2]);
+    issue_next(stage(0));
+    if (n_it > 1) issue_next(stage(1));
+    if (n_it > 2) issue_next(stage(2));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -339,11 +349,11 @@ void fa_fwd_kernel(const FwdParams p) {
     {
       bf16x8 qa[PF];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) qa[i] = a_frag(stg[0], i);
+      for (int i = 0; i < PF; ++i) qa[i] = a_frag(stage(0), i);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const bf16x8 a = qa[ks % PF];
-        if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(stg[0], ks + PF);
+        if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(stage(0), ks + PF);
         a_step(sA, 2 * ks, a);
         a_step(sA, 2 * ks + 1, a);
         __builtin_amdgcn_sched_barrier(0);
@@ -388,10 +398,10 @@ void fa_fwd_kernel(const FwdParams p) {
 
   // ---- epilogue: O = O / l, LSE = m * scale + ln(l) ----
   barrier_no_fence();
-  char FA_LDS* st = stg[0];
-  if (wave == 1) st = stg[1];
-  if (wave == 2) st = stg[2];
-  if (wave == 3) st = stg[3];
+  char FA_LDS* st = stage(0);
+  if (wave == 1) st = stage(1);
+  if (wave == 2) st = stage(2);
+  if (wave == 3) st = stage(3);
   __bf16* obase = (__bf16*)p.o + ((long)seq0 * p.Hq + h) * D;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
