@@ -203,7 +203,9 @@ def main():
             return sorted(windows)[1]
 
         for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
-                     "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64"):
+                     "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64",
+                     "bwd_causal_varlen16_hq32_hkv8_d128", "fwd_causal_b1_h16_n131072_d128",
+                     "bwd_causal_b1_h8_n65536_d128"):
             wl = I.WORKLOADS[name]
             if wl.varlen:
                 lens = I.draw_lengths(np.random.default_rng(wl.seed), wl.B, wl.len_lo, wl.len_hi)

@@ -83,7 +83,8 @@ class Workload:
         return float(np.float32(1.0 / math.sqrt(self.d)))
 
 
-# The five workloads (names say what they are).
+# Workloads (names say what they are): the five measured configurations, then
+# the packed GQA backward and two long-context runs.
 WORKLOADS = {
     "fwd_b1_h2_n256_d64": Workload(
         "fwd_b1_h2_n256_d64", "fwd", Hq=2, Hkv=2, d=64, causal=False, seed=1, B=1, N=256),
@@ -96,6 +97,15 @@ WORKLOADS = {
         B=16, varlen=True, len_lo=512, len_hi=16384),
     "bwd_causal_b2_h16_n8192_d128": Workload(
         "bwd_causal_b2_h16_n8192_d128", "bwd", Hq=16, Hkv=16, d=128, causal=True, seed=5, B=2, N=8192),
+    # the packed GQA workload's shapes and Q/K/V, backward (dO drawn after V)
+    "bwd_causal_varlen16_hq32_hkv8_d128": Workload(
+        "bwd_causal_varlen16_hq32_hkv8_d128", "bwd", Hq=32, Hkv=8, d=128, causal=True, seed=4,
+        B=16, varlen=True, len_lo=512, len_hi=16384),
+    # long context on one GPU
+    "fwd_causal_b1_h16_n131072_d128": Workload(
+        "fwd_causal_b1_h16_n131072_d128", "fwd", Hq=16, Hkv=16, d=128, causal=True, seed=6, B=1, N=131072),
+    "bwd_causal_b1_h8_n65536_d128": Workload(
+        "bwd_causal_b1_h8_n65536_d128", "bwd", Hq=8, Hkv=8, d=128, causal=True, seed=7, B=1, N=65536),
 }
 
 

@@ -10,4 +10,4 @@ no attention arithmetic.
   bruteforce.py  pure-Python loops with math.fsum, tiny inputs only
 """
 from .attention import (attention_forward, attention_backward, backward_rowdot,  # noqa: F401
-                        head_forward, head_backward, head_scores)
+                        head_forward, head_backward, head_backward_dq_rows, head_scores)

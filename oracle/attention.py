@@ -172,6 +172,23 @@ def head_backward(qh, kh, vh, doh, scale, causal):
     return dq, dk, dv
 
 
+def head_backward_dq_rows(qh, kh, vh, doh, scale, causal, rows):
+    """dQ of the selected rows of one (sequence, query head): [R, d].
+
+    Row i of dQ needs only row i of P, O and dO (the dS and dQ lines of the
+    definition above, for one i): P_i and O_i from the row-restricted forward,
+    dP_i = dO_i V^T, D_i = dO_i . O_i, dS_i = P_i (dP_i - D_i), dQ_i = scale dS_i K.
+    Used for sampled checks of sequences too long for whole heads.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    o_r, _, p_r = head_forward(qh, kh, vh, scale, causal, rows)
+    do_r = doh[rows]
+    dp_r = do_r @ vh.T
+    dd_r = np.sum(do_r * o_r, axis=1)
+    ds_r = p_r * (dp_r - dd_r[:, None])
+    return scale * (ds_r @ kh)
+
+
 def backward_rowdot(do: np.ndarray, o: np.ndarray) -> np.ndarray:
     """D_i = sum_k dO[i, h, k] O[i, h, k], shaped like the LSE ([B, Hq, N] or [Hq, T])."""
     d = np.sum(do * o, axis=-1)

@@ -320,3 +320,18 @@ def pin_gradient_invariants(fwd, bwd):
 
 ALL_FWD_PINS = [pin_bruteforce, pin_closed_forms, pin_invariants, pin_logsumexp, pin_reductions, pin_torch]
 ALL_BWD_PINS = [pin_finite_differences, pin_gradient_invariants, pin_reductions, pin_torch]
+
+
+# ---------------------------------------------------------------------------
+# row-sampled dQ (for sequences too long for whole heads)
+# ---------------------------------------------------------------------------
+
+def pin_dq_rows(dq_rows):
+    """dq_rows(qh, kh, vh, doh, scale, causal, rows) equals PyTorch fp64 autograd's dQ on those rows."""
+    rng = np.random.default_rng(23)
+    for (N, d, causal) in [(37, 16, True), (29, 8, False)]:
+        q, k, v, do = (rng.standard_normal((1, N, 1, d)) for _ in range(4))
+        *_, dq_t, _, _ = _torch_reference(q, k, v, do, 0.4, causal)
+        rows = np.array([0, 3, 17, N - 1])
+        dq = dq_rows(q[0, :, 0], k[0, :, 0], v[0, :, 0], do[0, :, 0], 0.4, causal, rows)
+        assert np.allclose(dq, dq_t[0, rows, 0], atol=1e-12, rtol=0), "row-sampled dQ vs torch autograd"

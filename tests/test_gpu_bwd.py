@@ -84,6 +84,78 @@ def test_backward_workload_full_size():
     assert np.max(np.abs(sv - so)) <= 0.02 * np.max(np.abs(so)) + 0.5
 
 
+def _f64(bits: np.ndarray) -> np.ndarray:
+    return I.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _sum_rules(x: I.Inputs, dk, dv, do, segments, label):
+    """Per (sequence, K/V head): sum_j dK_j = 0 and sum_j dV_j = sum over the group's query
+    heads of sum_i dO_i (rows of P sum to one). Sums in float64 on the GPU; any size."""
+    G = x.Hq // x.Hkv
+    for (a, b) in segments:
+        sk = dk[a:b].double().sum(dim=0)                         # [Hkv, d]
+        nk = dk[a:b].double().pow(2).sum(dim=0).sqrt()
+        sv = dv[a:b].double().sum(dim=0)
+        so = do[a:b].double().sum(dim=0).reshape(x.Hkv, G, -1).sum(dim=1)
+        assert bool((sk.abs() <= 0.05 * nk + 1e-3).all()), f"{label}: sum_j dK_j != 0 for tokens {a}..{b}"
+        assert float((sv - so).abs().max()) <= 0.02 * float(so.abs().max()) + 0.5, f"{label}: sum dV != sum dO"
+
+
+def _check_dq_rows(x: I.Inputs, dq, a, b, heads, label):
+    """dQ on sampled rows of one sequence (tokens a..b) against the row-sampled oracle."""
+    G = x.Hq // x.Hkv
+    rows = H.sampled_rows(n_first=64, n_last=64, stride=509)(0, b - a)
+    for h in heads:
+        g = h // G
+        ref = oracle.head_backward_dq_rows(_f64(x.q[a:b, h]), _f64(x.k[a:b, g]), _f64(x.v[a:b, g]),
+                                           _f64(x.do[a:b, h]), x.scale, x.causal, rows)
+        got = dq[a:b, h][torch.from_numpy(rows).to(dq.device)].double().cpu().numpy()
+        e = H.rel_fro(got, ref)
+        assert e <= H.GRAD_REL_FRO, f"{label}: dQ rows of head {h}: relative Frobenius error {e:.3e}"
+
+
+def test_backward_varlen_gqa_full_size():
+    """bwd_causal_varlen16_hq32_hkv8_d128 (16 packed sequences of 512..16384 tokens, 4 query heads per
+    K/V head): whole K/V groups of the two shortest sequences against the oracle, dQ on sampled rows of
+    the longest one, and the gradient sum rules on every (sequence, K/V head)."""
+    x = I.workload_inputs("bwd_causal_varlen16_hq32_hkv8_d128")
+    o, lse, dq, dk, dv = gpu_fwd_bwd(x)
+    cu = x.cu_seqlens
+    lens = np.diff(cu)
+    G = x.Hq // x.Hkv
+    for s in np.argsort(lens)[:2]:
+        a, b = int(cu[s]), int(cu[s + 1])
+        for g in (0, x.Hkv - 1):
+            kg, vg = _f64(x.k[a:b, g]), _f64(x.v[a:b, g])
+            rk, rv = np.zeros_like(kg), np.zeros_like(vg)
+            for h in range(g * G, (g + 1) * G):
+                rq, gk, gv = oracle.head_backward(_f64(x.q[a:b, h]), kg, vg, _f64(x.do[a:b, h]), x.scale, True)
+                rk += gk
+                rv += gv
+                e = H.rel_fro(dq[a:b, h].double().cpu().numpy(), rq)
+                assert e <= H.GRAD_REL_FRO, f"seq {s} head {h}: dQ relative Frobenius error {e:.3e}"
+            for name, got, ref in (("dK", dk[a:b, g], rk), ("dV", dv[a:b, g], rv)):
+                e = H.rel_fro(got.double().cpu().numpy(), ref)
+                assert e <= H.GRAD_REL_FRO, f"seq {s} K/V head {g}: {name} relative Frobenius error {e:.3e}"
+    s = int(np.argmax(lens))
+    _check_dq_rows(x, dq, int(cu[s]), int(cu[s + 1]), (0, x.Hq - 1), f"longest sequence {s}")
+    do = H.dev(x.do)
+    _sum_rules(x, dk, dv, do, [(int(cu[i]), int(cu[i + 1])) for i in range(len(lens)) if lens[i] > 0], "varlen")
+
+
+def test_backward_long_context():
+    """bwd_causal_b1_h8_n65536_d128: dQ on sampled rows of two heads, sum rules on every head."""
+    x = I.workload_inputs("bwd_causal_b1_h8_n65536_d128")
+    o, lse, dq, dk, dv = gpu_fwd_bwd(x)
+    N = x.N
+    dq2, dk2, dv2, do2 = (t.reshape(N, t.shape[2], t.shape[3]) for t in (dq, dk, dv, H.dev(x.do)))
+    xs = I.Inputs(q=x.q.reshape(N, x.Hq, x.d), k=x.k.reshape(N, x.Hkv, x.d), v=x.v.reshape(N, x.Hkv, x.d),
+                  do=x.do.reshape(N, x.Hq, x.d), cu_seqlens=None, B=1, N=N, Hq=x.Hq, Hkv=x.Hkv, d=x.d,
+                  causal=x.causal, scale=x.scale)
+    _check_dq_rows(xs, dq2, 0, N, (0, x.Hq - 1), "N=65536")
+    _sum_rules(xs, dk2, dv2, do2, [(0, N)], "N=65536")
+
+
 def test_backward_deterministic_and_fully_written():
     x = I.make_inputs(1, 300, 4, 2, 128, True, seed=21, with_do=True)
     o, lse, dq, dk, dv = gpu_fwd_bwd(x)

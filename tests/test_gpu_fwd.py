@@ -53,7 +53,7 @@ def test_forward_workload_small_d64():
 
 
 @pytest.mark.parametrize("name", ["fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
-                                  "fwd_causal_varlen16_hq32_hkv8_d128"])
+                                  "fwd_causal_varlen16_hq32_hkv8_d128", "fwd_causal_b1_h16_n131072_d128"])
 def test_forward_workload_sampled(name):
     """Full-size workloads, checked on sampled rows of every (sequence, head)."""
     x = I.workload_inputs(name)

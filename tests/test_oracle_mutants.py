@@ -70,3 +70,22 @@ def test_backward_mutant_is_caught(name):
     fwd, bwd = _mutant(*BWD_MUTANTS[name])
     order = [pins.pin_gradient_invariants, pins.pin_torch, pins.pin_reductions, pins.pin_finite_differences]
     assert _caught(order, fwd, bwd) is not None, f"mutant {name} passed every backward pin"
+
+
+DQ_ROWS_MUTANTS = {
+    "rows_ds_sign_of_d": ("ds_r = p_r * (dp_r - dd_r[:, None])", "ds_r = p_r * (dp_r + dd_r[:, None])"),
+    "rows_d_uses_do_twice": ("dd_r = np.sum(do_r * o_r, axis=1)", "dd_r = np.sum(do_r * do_r, axis=1)"),
+    "rows_drops_scale": ("return scale * (ds_r @ kh)", "return (ds_r @ kh)"),
+    "rows_uses_v": ("return scale * (ds_r @ kh)", "return scale * (ds_r @ vh)"),
+    "rows_unselected_do": ("do_r = doh[rows]", "do_r = doh[:len(rows)]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DQ_ROWS_MUTANTS))
+def test_dq_rows_mutant_is_caught(name):
+    old, new = DQ_ROWS_MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    with pytest.raises(AssertionError):
+        pins.pin_dq_rows(mod.head_backward_dq_rows)

@@ -57,3 +57,9 @@ def test_empty_sequence_is_skipped():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     dq, dk, dv = oracle.attention_backward(q, k, v, rng.standard_normal((5, 2, 4)), 0.5, True, cu)
     assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+
+
+
+def test_dq_rows_match_torch_autograd():
+    """The row-sampled dQ equals PyTorch fp64 autograd's dQ on those rows."""
+    pins.pin_dq_rows(oracle.head_backward_dq_rows)
