@@ -58,10 +58,10 @@ def source_hash(names):
 
 
 KERNEL_SOURCES = {
-    "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_tiles.h"],
-    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_tiles.h"],
-    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_tiles.h"],
-    "bwd_prep_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_tiles.h"],
+    "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
+    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
+    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
+    "bwd_prep_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
 }
 
 

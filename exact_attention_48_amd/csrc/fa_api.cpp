@@ -18,15 +18,28 @@ inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 namespace fa {
 
+// Workspace layout: D_i | LSE_i * log2(e) (each laid out like the LSE) | for
+// packed batches, the dK/dV schedule (8 x (B + 1) int32 at most).
+size_t bwd_lse_bytes(long B, long Hq, long N) {
+  const size_t rows = (size_t)B * (size_t)N;          // >= T for packed batches
+  return round256(rows * (size_t)Hq * sizeof(float));
+}
+
 size_t bwd_workspace_bytes(long B, long Hq, long Hkv, long N, int d, int causal, int varlen) {
   (void)Hkv;
   (void)causal;
-  (void)varlen;
-  if (B <= 0 || N <= 0 || Hq <= 0) return 0;
   (void)d;
-  const size_t rows = (size_t)B * (size_t)N;          // >= T for packed batches
-  // D_i and LSE_i * log2(e), each laid out like the LSE
-  return 2 * round256(rows * (size_t)Hq * sizeof(float));
+  if (B <= 0 || N <= 0 || Hq <= 0) return 0;
+  const size_t sched = varlen ? round256((size_t)8 * (size_t)(B + 1) * sizeof(int)) : 0;
+  return 2 * bwd_lse_bytes(B, Hq, N) + sched;
+}
+
+// Work is dealt to the 8 XCDs by (K/V head, tile residue): with 8 / gcd(Hkv, 8)
+// residues every XCD gets the same share of every sequence.
+int xcd_chunks(int Hkv) {
+  int g = 8;
+  while (Hkv % g) g >>= 1;                             // gcd(Hkv, 8)
+  return 8 / g;
 }
 
 }  // namespace fa
@@ -66,7 +79,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   p.G = Hq / Hkv;
   p.N = N;
   p.lpt = options ? options->lpt_order : 1;
-  p.xcd_group = p.G;
+  p.kv_chunks = fa::xcd_chunks(Hkv);
   p.scale_log2 = softmax_scale * kLog2eF;
   p.tau = options ? options->rescale_tau : kDefaultTau;
   const int expmode = options ? options->exp_mode : FA_EXP_HW;
@@ -107,8 +120,11 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   p.dk = dk;
   p.dv = dv;
   p.cu_seqlens = cu_seqlens;
+  const size_t half = fa::bwd_lse_bytes(B, Hq, N);
   p.dsum = (float*)workspace;
-  p.lse2 = (float*)((char*)workspace + needed / 2);
+  p.lse2 = (float*)((char*)workspace + half);
+  p.kt_prefix = cu_seqlens ? (int*)((char*)workspace + 2 * half) : nullptr;
+  p.kv_chunks = fa::xcd_chunks(Hkv);
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -9,7 +9,8 @@
 //
 // Three kernels, all on the caller's stream:
 //   1. bwd_prep_kernel: D_i = rowsum(dO o O) and LSE_i * log2(e), fp32, into
-//      the workspace (HBM-bound, one pass).
+//      the workspace (HBM-bound, one pass); for packed batches also
+//      bwd_sched_kernel, the order in which kernel 2 takes its work.
 //   2. bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128-key tile),
 //      one wave per SIMD. Each wave keeps 32 keys' K and V fragments and their
 //      dK/dV accumulators in registers and streams the 64-row Q / dO tiles of
@@ -40,6 +41,7 @@
 
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_order.h"
 #include "fa_tiles.h"
 
 namespace fa {
@@ -92,6 +94,43 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, long t
   }
 }
 
+// Schedule of the dK/dV kernel for packed batches: with c = 8 / gcd(Hkv, 8) and
+// n_kt(s) the 128-key tiles of sequence s, kt_prefix[i * (B + 1) + s] counts the
+// key tiles kt < n_kt(s') with kt = i (mod c) over the sequences s' < s (i < c).
+// One workgroup; thread t scans a contiguous run of sequences.
+__global__ __launch_bounds__(256) void bwd_sched_kernel(const int32_t* cu, int B, int c, int* out) {
+  __shared__ int part[256];
+  const int t = threadIdx.x;
+  const int per = (B + 255) / 256;
+  const int s0 = min(B, t * per), s1 = min(B, s0 + per);
+  auto count = [&](int s, int i) {
+    const int nkt = (cu[s + 1] - cu[s] + KV_BN - 1) / KV_BN;
+    return nkt > i ? (nkt - i + c - 1) / c : 0;
+  };
+  for (int i = 0; i < c; ++i) {
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) sum += count(s, i);
+    part[t] = sum;
+    __syncthreads();
+    if (t == 0) {
+      int run = 0;
+      for (int k = 0; k < 256; ++k) {
+        const int x = part[k];
+        part[k] = run;
+        run += x;
+      }
+      out[i * (B + 1) + B] = run;
+    }
+    __syncthreads();
+    int run = part[t];
+    for (int s = s0; s < s1; ++s) {
+      out[i * (B + 1) + s] = run;
+      run += count(s, i);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. dK, dV: KV-major
 // ---------------------------------------------------------------------------
@@ -125,14 +164,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
-  // work item: level-major (key tile 0 first: under causal masking it sees the
-  // most query tiles), then (sequence, K/V head)
-  const int per_level = p.B * p.Hkv;
-  const int w = blockIdx.x;
-  const int kt = w / per_level;
-  const int rr = w - kt * per_level;
-  const int s = rr / p.Hkv;
-  const int hkv = rr - s * p.Hkv;
+  // ---- work item -> (sequence s, K/V head hkv, key tile kt), in the order
+  // fa_order.h describes ----
+  TileItem item;
+  if constexpr (VARLEN) {
+    if (!kv_item_xcd(blockIdx.x, p.B, p.Hkv, p.kv_chunks, p.kt_prefix, item)) return;
+  } else {
+    if (!kv_item_level(blockIdx.x, p.B, p.Hkv, (p.N + KV_BN - 1) / KV_BN, item)) return;
+  }
+  const int s = item.s, hkv = item.h, kt = item.t;
 
   int seq0, L, T = 0;
   if constexpr (VARLEN) {
@@ -407,7 +447,7 @@ struct QStage {
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
-void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
+void bwd_dq_kernel(const BwdParams p, int n_qtiles) {
   using S = QStage<D>;
   using RC = RowCopy<D, DQ_BN>;
   constexpr int KSTEPS = D / 16;
@@ -424,18 +464,15 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles, int xcd_group) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
-  int w = blockIdx.x;
-  if (xcd_group > 0) {
-    const int xcd = w & 7, j = w >> 3;
-    w = (8 * (j / xcd_group) + xcd) * xcd_group + (j % xcd_group);
+  // work item -> (sequence s, query head h, query tile qt), in the order
+  // fa_order.h describes, heaviest (last) query tiles first
+  TileItem item;
+  if constexpr (VARLEN) {
+    if (!q_item_xcd(blockIdx.x, p.B, p.Hkv, p.G, p.kv_chunks, n_qtiles, true, item)) return;
+  } else {
+    if (!q_item_level(blockIdx.x, p.B, p.Hq, p.G, n_qtiles, true, item)) return;
   }
-  const int per_level = p.B * p.Hq;
-  if (w >= per_level * n_qtiles) return;
-  const int lvl = w / per_level;
-  const int rr = w - lvl * per_level;
-  const int s = rr / p.Hq;
-  const int h = rr - s * p.Hq;
-  const int qt = n_qtiles - 1 - lvl;            // heaviest (last) query tiles first
+  const int s = item.s, h = item.h, qt = item.t;
   const int hkv = h / p.G;
 
   int seq0, L, T = 0;
@@ -670,19 +707,24 @@ static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t strea
     hipLaunchKernelGGL((bwd_prep_kernel<D, VARLEN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        stream, p, rows);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (VARLEN) {
+      hipLaunchKernelGGL(bwd_sched_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.B, p.kv_chunks,
+                         p.kt_prefix);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if (stages & 2) {
     const int n_kt = (p.N + KV_BN - 1) / KV_BN;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3(n_kt * p.B * p.Hkv), dim3(NTHREADS), 0, stream,
-                       p);
+    const long grid = VARLEN ? kv_grid_xcd(p.B, p.Hkv, p.kv_chunks, n_kt) : kv_grid_level(p.B, p.Hkv, n_kt);
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4) {
     const int n_qt = (p.N + DQ_BM - 1) / DQ_BM;
-    const int items = n_qt * p.B * p.Hq;
-    const int xg = p.G;
-    const int grid = (items + 8 * xg - 1) / (8 * xg) * (8 * xg);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3(grid), dim3(NTHREADS), 0, stream, p, n_qt, xg);
+    const long grid = VARLEN ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, n_qt) : q_grid_level(p.B, p.Hq, p.G, n_qt);
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p, n_qt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

@@ -51,6 +51,7 @@
 // (workgroups are dealt to the 8 XCDs round-robin) so they share its L2.
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_order.h"
 #include "fa_tiles.h"
 
 namespace fa {
@@ -101,20 +102,15 @@ void fa_fwd_kernel(const FwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
-  // ---- work item -> (sequence, head, query tile) ----
-  int w = blockIdx.x;
-  if (p.xcd_group > 0) {
-    // workgroup i runs on XCD i % 8; give XCD x the item groups x, x+8, ...
-    const int xcd = w & 7, j = w >> 3;
-    w = (8 * (j / p.xcd_group) + xcd) * p.xcd_group + (j % p.xcd_group);
+  // ---- work item -> (sequence s, query head h, query tile qt), in the order
+  // fa_order.h describes ----
+  TileItem item;
+  if constexpr (VARLEN) {
+    if (!q_item_xcd(blockIdx.x, p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles, p.lpt, item)) return;
+  } else {
+    if (!q_item_level(blockIdx.x, p.B, p.Hq, p.G, p.n_qtiles, p.lpt, item)) return;
   }
-  if (w >= p.n_items) return;
-  const int per_level = p.B * p.Hq;
-  const int lvl = w / per_level;
-  const int rr = w - lvl * per_level;
-  const int s = rr / p.Hq;
-  const int h = rr - s * p.Hq;
-  const int qt = p.lpt ? (p.n_qtiles - 1 - lvl) : lvl;
+  const int s = item.s, h = item.h, qt = item.t;
   const int hkv = h / p.G;
 
   int seq0, L;
@@ -449,13 +445,11 @@ int fwd_block_m() { return BM; }
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream) {
   p.n_qtiles = (p.N + BM - 1) / BM;
-  p.n_items = p.n_qtiles * p.B * p.Hq;
-  if (p.n_items == 0) return hipSuccess;
-  int grid = p.n_items;
-  if (p.xcd_group > 0) {
-    const int g8 = 8 * p.xcd_group;
-    grid = (p.n_items + g8 - 1) / g8 * g8;
-  }
+  const long grid_l = varlen ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles)
+                             : q_grid_level(p.B, p.Hq, p.G, p.n_qtiles);
+  if (grid_l == 0) return hipSuccess;
+  if (grid_l > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const int grid = (int)grid_l;
   if (d == 128) return launch_fwd_d<128>(p, grid, causal, varlen, expmode, stream);
   return launch_fwd_d<64>(p, grid, causal, varlen, expmode, stream);
 }

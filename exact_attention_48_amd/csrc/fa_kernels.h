@@ -15,8 +15,7 @@ struct FwdParams {
   const int32_t* cu_seqlens;   // nullptr for uniform batches
   int B, Hq, Hkv, G, N;
   int n_qtiles;                // query tiles per sequence (set by fwd_launch)
-  int n_items;                 // B * Hq * n_qtiles (set by fwd_launch)
-  int xcd_group;               // consecutive work items kept on one XCD (0 = off)
+  int kv_chunks;               // query-tile residues per (sequence, K/V head): 8 / gcd(Hkv, 8)
   int lpt;                     // 1: heaviest query tiles first
   float scale_log2;            // softmax_scale * log2(e)
   float tau;                   // conditional rescale threshold (log2 units)
@@ -38,6 +37,8 @@ struct BwdParams {
   const int32_t* cu_seqlens;
   float* dsum;                 // workspace: D_i = rowsum(dO * O), laid out like LSE
   float* lse2;                 // workspace: LSE_i * log2(e), laid out like LSE
+  int* kt_prefix;              // workspace (packed batches): dK/dV schedule, see bwd_sched_kernel
+  int kv_chunks;               // tile residues per (sequence, K/V head): 8 / gcd(Hkv, 8)
   int B, Hq, Hkv, G, N;
   float scale;
   float scale_log2;
@@ -45,5 +46,7 @@ struct BwdParams {
 
 hipError_t bwd_launch(BwdParams p, int d, int causal, int varlen, int stages, hipStream_t stream);
 size_t bwd_workspace_bytes(long B, long Hq, long Hkv, long N, int d, int causal, int varlen);
+size_t bwd_lse_bytes(long B, long Hq, long N);
+int xcd_chunks(int Hkv);
 
 }  // namespace fa

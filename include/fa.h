@@ -128,7 +128,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 
 /* Stages of the backward pass, for fa_bwd_ex. */
 typedef enum {
-    FA_BWD_PREPROCESS = 1,  /* D_i = rowsum(dO o O) and LSE_i * log2(e) into the workspace */
+    FA_BWD_PREPROCESS = 1,  /* D_i = rowsum(dO o O) and LSE_i * log2(e) into the workspace; for
+                               packed batches also the order in which DKDV takes its work */
     FA_BWD_DKDV = 2,        /* dK and dV (read the workspace) */
     FA_BWD_DQ = 4,          /* dQ (reads the workspace) */
     FA_BWD_ALL = 7

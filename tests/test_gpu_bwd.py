@@ -66,6 +66,19 @@ def test_backward_varlen_gqa(causal, d):
     check_grads(x, dq, dk, dv, f"varlen d={d} causal={causal}")
 
 
+# Packed batches split each (sequence, K/V head)'s tiles over 8 / gcd(Hkv, 8)
+# XCDs: 1 way for Hkv = 8, 8 ways for Hkv = 3; the 700-token sequence spans six
+# 128-key tiles and three 256-query tiles.
+@pytest.mark.parametrize("heads", [(8, 8), (6, 3)], ids=["hq8_hkv8", "hq6_hkv3"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_head_splits(heads, causal):
+    Hq, Hkv = heads
+    lens = [700, 1, 0, 257, 129, 383]
+    x = I.make_inputs(0, 0, Hq, Hkv, 128, causal, seed=95 + Hkv, with_do=True, lengths=lens)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(x)
+    check_grads(x, dq, dk, dv, f"varlen Hq={Hq} Hkv={Hkv} causal={causal}")
+
+
 def test_backward_workload_full_size():
     """bwd_causal_b2_h16_n8192_d128: two whole heads against the oracle, invariants on all heads."""
     x = I.workload_inputs("bwd_causal_b2_h16_n8192_d128")

@@ -44,6 +44,19 @@ def test_forward_varlen_gqa(causal, d):
     H.check_forward(o, lse, o_ref, lse_ref, f"varlen d={d} causal={causal}")
 
 
+# Packed batches split each (sequence, K/V head)'s query tiles over
+# 8 / gcd(Hkv, 8) XCDs (1 way for Hkv = 8, 8 ways for Hkv = 3).
+@pytest.mark.parametrize("heads", [(8, 8), (6, 3)], ids=["hq8_hkv8", "hq6_hkv3"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_varlen_head_splits(heads, causal):
+    Hq, Hkv = heads
+    lens = [700, 1, 0, 257, 129, 383]
+    x = I.make_inputs(0, 0, Hq, Hkv, 128, causal, seed=81 + Hkv, lengths=lens)
+    *_, o, lse = H.gpu_forward(x)
+    o_ref, lse_ref = H.oracle_forward(x)
+    H.check_forward(o, lse, o_ref, lse_ref, f"varlen Hq={Hq} Hkv={Hkv} causal={causal}")
+
+
 def test_forward_workload_small_d64():
     """fwd_b1_h2_n256_d64, all rows."""
     x = I.workload_inputs("fwd_b1_h2_n256_d64")
