@@ -6,8 +6,10 @@ never imports it and shares no code with it; the only module both sides use
 is the seeded input generator ``exact_attention_48_amd.inputs``, which holds
 no attention arithmetic.
 
-  attention.py   float64 NumPy attention forward/backward (the definition)
+  attention.py   float64 NumPy attention forward/backward (the definition), split-KV
+                 partial results and their merge
   bruteforce.py  pure-Python loops with math.fsum, tiny inputs only
 """
 from .attention import (attention_forward, attention_backward, backward_rowdot,  # noqa: F401
-                        head_forward, head_backward, head_backward_dq_rows, head_scores)
+                        head_forward, head_backward, head_backward_dq_rows, head_scores,
+                        attention_forward_split, head_forward_keys, merge_partials, split_chunk)

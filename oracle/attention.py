@@ -195,3 +195,98 @@ def backward_rowdot(do: np.ndarray, o: np.ndarray) -> np.ndarray:
     if d.ndim == 3:
         return np.transpose(d, (0, 2, 1)).copy()
     return d.T.copy()
+
+
+# ---------------------------------------------------------------------------
+# Split-KV partial results and their merge.
+#
+# Attention over all keys equals the merge of attention over disjoint key
+# chunks: with LSE_p the log-sum-exp of the scores of chunk p and O_p that
+# chunk's softmax-weighted sum of V, LSE = ln sum_p exp(LSE_p) and
+# O = sum_p exp(LSE_p - LSE) O_p. This is the combination step of the online
+# softmax that tiling relies on (podcast.app episode page, description,
+# second paragraph), applied across chunks instead of tiles; the same step
+# joins the partial results of blockwise ring attention (that page's source
+# list, "Ring Attention with Blockwise Transformers for Near-Infinite
+# Context"). The pages give no layout or chunking for it; the readings here:
+#   * queries and keys may differ in number (Nq <= Nk when causal); query i
+#     sits at key position i + Nk - Nq, so the last query sees every key;
+#   * chunk p holds keys p*C .. min((p+1)*C, Nk) - 1 with C = ceil(Nk / n);
+#   * a row that sees no key of a chunk has LSE_p = -inf and O_p = 0.
+# ---------------------------------------------------------------------------
+
+def split_chunk(nk: int, n_splits: int, p: int) -> Tuple[int, int]:
+    """Key range [begin, end) of chunk p (empty when begin >= end)."""
+    c = -(-nk // n_splits)
+    return min(p * c, nk), min((p + 1) * c, nk)
+
+
+def head_forward_keys(qh, kh, vh, scale, causal, q_off, kb, ke):
+    """Attention of every query of one head over keys kb .. ke-1 only.
+
+    qh [Nq, d], kh/vh [Nk, d]; query i is at key position i + q_off. Returns
+    (O [Nq, d], LSE [Nq]) with O = 0, LSE = -inf for rows seeing no key.
+    """
+    nq = qh.shape[0]
+    o = np.zeros((nq, qh.shape[1]))
+    lse = np.full(nq, -np.inf)
+    if ke <= kb:
+        return o, lse
+    s = scale * (qh @ kh[kb:ke].T)
+    if causal:
+        j = np.arange(kb, ke)
+        s[j[None, :] > (np.arange(nq) + q_off)[:, None]] = -np.inf
+    live = np.isfinite(s).any(axis=1)
+    if live.any():
+        sl = s[live]
+        m = sl.max(axis=1)
+        e = np.exp(sl - m[:, None])
+        l = e.sum(axis=1)
+        o[live] = (e / l[:, None]) @ vh[kb:ke]
+        lse[live] = m + np.log(l)
+    return o, lse
+
+
+def attention_forward_split(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+                            n_splits: int):
+    """Partial attention over each of n_splits key chunks (uniform batches).
+
+    Q [B, Nq, Hq, d], K/V [B, Nk, Hkv, d]. Returns O_part [n, B, Nq, Hq, d]
+    and LSE_part [n, B, Hq, Nq] in float64 (readings above).
+    """
+    B, nq, Hq, d = q.shape
+    nk, Hkv = k.shape[1], k.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if causal and nq > nk:
+        raise ValueError("causal needs Nq <= Nk")
+    G = Hq // Hkv
+    o_part = np.zeros((n_splits, B, nq, Hq, d))
+    lse_part = np.full((n_splits, B, Hq, nq), -np.inf)
+    for p in range(n_splits):
+        kb, ke = split_chunk(nk, n_splits, p)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G
+                oh, lh = head_forward_keys(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal,
+                                           nk - nq, kb, ke)
+                o_part[p, b, :, h, :] = oh
+                lse_part[p, b, h, :] = lh
+    return o_part, lse_part
+
+
+def merge_partials(o_part: np.ndarray, lse_part: np.ndarray):
+    """Merge partial results: LSE = ln sum_p exp(LSE_p), O = sum_p exp(LSE_p - LSE) O_p.
+
+    o_part [n, B, N, H, d], lse_part [n, B, H, N]; rows whose every LSE_p is
+    -inf get LSE = -inf and O = 0. Returns (O [B, N, H, d], LSE [B, H, N]).
+    """
+    m = lse_part.max(axis=0)
+    dead = ~np.isfinite(m)
+    m_safe = np.where(dead, 0.0, m)
+    w = np.exp(lse_part - m_safe[None])                     # exp(-inf) = 0 for empty parts
+    tot = w.sum(axis=0)
+    lse = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, tot)))
+    coef = np.where(dead[None], 0.0, w / np.where(dead, 1.0, tot)[None])   # [n, B, H, N]
+    o = np.einsum("pbhn,pbnhd->bnhd", coef, o_part)
+    return o, lse

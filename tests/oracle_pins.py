@@ -335,3 +335,79 @@ def pin_dq_rows(dq_rows):
         rows = np.array([0, 3, 17, N - 1])
         dq = dq_rows(q[0, :, 0], k[0, :, 0], v[0, :, 0], do[0, :, 0], 0.4, causal, rows)
         assert np.allclose(dq, dq_t[0, rows, 0], atol=1e-12, rtol=0), "row-sampled dQ vs torch autograd"
+
+
+# ---------------------------------------------------------------------------
+# split-KV partial results and their merge
+# ---------------------------------------------------------------------------
+
+SPLIT_CASES = [
+    # (B, Nq, Nk, Hq, Hkv, d, causal, n_splits)
+    (1, 7, 7, 2, 1, 4, True, 3),
+    (2, 5, 9, 2, 2, 3, True, 4),
+    (1, 3, 8, 4, 2, 5, False, 3),
+    (1, 1, 9, 2, 1, 4, True, 5),
+    (1, 6, 6, 1, 1, 3, True, 9),    # more chunks than keys: some are empty
+]
+
+
+def _torch_chunk(q, k, v, scale, causal, kb, ke):
+    """LSE_p and O_p of keys kb..ke-1 by PyTorch fp64 logsumexp / softmax on masked scores."""
+    import torch
+    B, nq, Hq, d = q.shape
+    nk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    tq = torch.tensor(q).permute(0, 2, 1, 3)
+    tk = torch.tensor(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    tv = torch.tensor(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    s = torch.matmul(tq, tk.transpose(-1, -2)) * scale                     # [B, Hq, nq, nk]
+    key = torch.arange(nk)[None, :]
+    dead = (key < kb) | (key >= ke)
+    if causal:
+        dead = dead | (key > torch.arange(nq)[:, None] + (nk - nq))
+    s = s.masked_fill(dead, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    p = torch.softmax(s, dim=-1)
+    o = torch.nan_to_num(torch.matmul(p, tv), nan=0.0)                     # rows with no key: 0
+    return o.permute(0, 2, 1, 3).numpy(), lse.numpy()
+
+
+def pin_split(split, merge):
+    """split(q, k, v, scale, causal, n) -> (O_part, LSE_part); merge(O_part, LSE_part) -> (O, LSE).
+
+    Merged partials equal brute-force attention (pure Python) of the whole key
+    range, with query i of Nq at key position i + Nk - Nq (brute force on the
+    Nk-token sequence, last Nq rows); each part equals PyTorch's logsumexp /
+    softmax restricted to keys p*C .. (p+1)*C - 1, C = ceil(Nk / n); rows that
+    see no key of a part hold LSE = -inf, O = 0; merging one part, or a part
+    with an all -inf one, gives that part back.
+    """
+    rng = np.random.default_rng(29)
+    scale = 0.41
+    for (B, nq, nk, Hq, Hkv, d, causal, n) in SPLIT_CASES:
+        q, k, v = _rand(rng, B, nq, Hq, d), _rand(rng, B, nk, Hkv, d), _rand(rng, B, nk, Hkv, d)
+        o_part, lse_part = split(q, k, v, scale, causal, n)
+        assert o_part.shape == (n, B, nq, Hq, d) and lse_part.shape == (n, B, Hq, nq)
+        o, lse = merge(o_part, lse_part)
+        q_full = np.concatenate([_rand(rng, B, nk - nq, Hq, d), q], axis=1)
+        ob, lb = bruteforce.forward(q_full.tolist(), k.tolist(), v.tolist(), scale, causal)
+        ob = np.array(ob)[:, nk - nq:]
+        lb = np.array(lb)[:, :, nk - nq:]
+        assert np.max(np.abs(o - ob)) < TOL, ("merged O vs brute force", B, nq, nk, causal, n)
+        assert np.max(np.abs(lse - lb)) < TOL, ("merged LSE vs brute force", B, nq, nk, causal, n)
+        c = math.ceil(nk / n)
+        for p in range(n):
+            kb, ke = min(p * c, nk), min((p + 1) * c, nk)
+            ot, lt = _torch_chunk(q, k, v, scale, causal, kb, ke)
+            both_dead = np.isneginf(lt) & np.isneginf(lse_part[p])
+            assert np.all(both_dead | (np.abs(lse_part[p] - lt) < TOL)), ("part LSE vs torch", p, kb, ke)
+            assert np.max(np.abs(o_part[p] - ot)) < TOL, ("part O vs torch", p, kb, ke)
+            dead_rows = np.isneginf(lse_part[p])                            # [B, Hq, nq]
+            assert np.all(o_part[p].transpose(0, 2, 1, 3)[dead_rows] == 0.0), "dead rows must hold O = 0"
+        o1, l1 = merge(o_part[:1], lse_part[:1])
+        assert np.array_equal(l1, lse_part[0]) and np.array_equal(o1, o_part[0]), "merge of one part"
+    # a part that is -inf everywhere leaves the other untouched
+    o_a = _rand(rng, 1, 3, 2, 4)
+    l_a = _rand(rng, 1, 2, 3)
+    o_m, l_m = merge(np.stack([o_a, np.zeros_like(o_a)]), np.stack([l_a, np.full_like(l_a, -np.inf)]))
+    assert np.array_equal(l_m, l_a) and np.allclose(o_m, o_a, rtol=0, atol=1e-15), "merge with an empty part"

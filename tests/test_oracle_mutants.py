@@ -89,3 +89,31 @@ def test_dq_rows_mutant_is_caught(name):
     exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
     with pytest.raises(AssertionError):
         pins.pin_dq_rows(mod.head_backward_dq_rows)
+
+
+SPLIT_MUTANTS = {
+    "chunk_size_floor": ("c = -(-nk // n_splits)", "c = nk // n_splits"),
+    "query_offset_sign": ("nk - nq, kb, ke)", "nq - nk, kb, ke)"),
+    "chunk_mask_includes_diagonal": ("s[j[None, :] > (np.arange(nq) + q_off)[:, None]] = -np.inf",
+                                     "s[j[None, :] >= (np.arange(nq) + q_off)[:, None]] = -np.inf"),
+    "chunk_positions_local": ("j = np.arange(kb, ke)", "j = np.arange(0, ke - kb)"),
+    "dead_rows_not_skipped": ("live = np.isfinite(s).any(axis=1)", "live = np.ones(nq, dtype=bool)"),
+    "chunk_lse_drops_max": ("lse[live] = m + np.log(l)", "lse[live] = np.log(l)"),
+    "merge_weight_sign": ("w = np.exp(lse_part - m_safe[None])", "w = np.exp(m_safe[None] - lse_part)"),
+    "merge_unnormalised": ("coef = np.where(dead[None], 0.0, w / np.where(dead, 1.0, tot)[None])",
+                           "coef = np.where(dead[None], 0.0, w)"),
+    "merge_lse_drops_max": ("lse = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, tot)))",
+                            "lse = np.where(dead, -np.inf, np.log(np.where(dead, 1.0, tot)))"),
+    "merge_takes_max_part": ("o = np.einsum(\"pbhn,pbnhd->bnhd\", coef, o_part)",
+                             "o = o_part[np.argmax(lse_part.max(axis=(1, 2, 3)))]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_MUTANTS))
+def test_split_mutant_is_caught(name):
+    old, new = SPLIT_MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    with pytest.raises(AssertionError):
+        pins.pin_split(mod.attention_forward_split, mod.merge_partials)

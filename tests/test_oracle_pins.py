@@ -63,3 +63,7 @@ def test_empty_sequence_is_skipped():
 def test_dq_rows_match_torch_autograd():
     """The row-sampled dQ equals PyTorch fp64 autograd's dQ on those rows."""
     pins.pin_dq_rows(oracle.head_backward_dq_rows)
+
+
+def test_split_and_merge_pins():
+    pins.pin_split(oracle.attention_forward_split, oracle.merge_partials)
