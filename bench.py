@@ -248,6 +248,35 @@ def main():
             del qw, kw, vw, ow, lse_w
             torch.cuda.empty_cache()
 
+        # split-KV partial results + merge: 512 queries against 131072 keys
+        name = "split_causal_b1_hq32_hkv8_nq512_nk131072_d128"
+        wl = I.WORKLOADS[name]
+        Bs, Nq, Nk, n = wl.B, wl.N, wl.Nk, wl.n_splits
+        qw = rnd((Bs, Nq, wl.Hq, wl.d), wl.seed * 10 + 1)
+        kw, vw = rnd((Bs, Nk, wl.Hkv, wl.d), wl.seed * 10 + 2), rnd((Bs, Nk, wl.Hkv, wl.d), wl.seed * 10 + 3)
+        opw = torch.empty((n, Bs, Nq, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+        lpw = torch.empty((n, Bs, wl.Hq, Nq), dtype=torch.float32, device=dev)
+        ow = torch.empty((Bs, Nq, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+        lw = torch.empty((Bs, wl.Hq, Nq), dtype=torch.float32, device=dev)
+        split = lambda m: capi.fa_fwd_split(qw, kw, vw, opw, lpw, Bs, wl.Hq, wl.Hkv, Nq, Nk, wl.d, int(wl.causal),
+                                            wl.scale, m, stream)
+        merge = lambda: capi.fa_merge(opw, lpw, ow, lw, n, Bs, wl.Hq, Nq, wl.d, stream)
+        fl = 4.0 * wl.Hq * wl.d * Bs * I.visible_pairs(Nq, Nk, wl.causal)
+        ms_1 = time_it(lambda: split(1), 5)          # one chunk: 2 query tiles x 32 heads = 64 workgroups
+        ms_s = time_it(lambda: split(n), 5)
+        ms_m = time_it(merge, 20)
+        rows = Bs * wl.Hq * Nq
+        merge_bytes = n * rows * (wl.d + 1) * 4 + rows * (wl.d * 2 + 4)
+        workloads[name] = {
+            "one_chunk_ms": round(ms_1, 4), "one_chunk_tflops": round(fl / (ms_1 * 1e-3) / 1e12, 1),
+            "split_ms": round(ms_s, 4), "split_tflops": round(fl / (ms_s * 1e-3) / 1e12, 1),
+            "merge_ms": round(ms_m, 4), "merge_gbs": round(merge_bytes / (ms_m * 1e-3) / 1e9, 1),
+            "split_plus_merge_tflops": round(fl / ((ms_s + ms_m) * 1e-3) / 1e12, 1),
+            "split_plus_merge_frac_of_peak": round(fl / ((ms_s + ms_m) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+        del qw, kw, vw, opw, lpw, ow, lw
+        torch.cuda.empty_cache()
+
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
     if not args.no_cpu_baseline:

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libfa.so")
 ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip"]
 
 
 def hipcc() -> str:

@@ -28,8 +28,8 @@ FA_BWD_DKDV = 2
 FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_status_string",
-            "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_split", "fa_merge",
+            "fa_status_string", "fa_version")
 
 
 class FaOptions(ctypes.Structure):
@@ -66,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = ci
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
     lib.fa_bwd_ex.restype = ci
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_fwd_split.restype = ci
+    lib.fa_merge.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    lib.fa_merge.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -142,4 +146,22 @@ def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B: int, Hq: int, Hkv: int, N: i
                           _ptr(workspace), int(workspace_bytes), int(stages), _stream(stream))
     if check and st != FA_OK:
         raise FaError(st, "fa_bwd_ex")
+    return st
+
+
+def fa_fwd_split(q, k, v, o_part, lse_part, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, causal: int,
+                 softmax_scale: float, n_splits: int, stream=None, check: bool = True) -> int:
+    st = load().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq, Hkv, Nq, Nk, d,
+                             int(causal), float(softmax_scale), int(n_splits), _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
+    return st
+
+
+def fa_merge(o_part, lse_part, o, lse, n_parts: int, B: int, H: int, N: int, d: int, stream=None,
+             check: bool = True) -> int:
+    st = load().fa_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), int(n_parts), B, H, N, d,
+                         _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_merge")
     return st

@@ -93,6 +93,45 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, nullptr, stream);
 }
 
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                       int n_splits, void* stream) {
+  fa_status st = fa::check_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale,
+                                 n_splits);
+  if (st != FA_OK) return st;
+  if (B == 0 || Nq == 0) return FA_OK;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.N = Nq;
+  p.lpt = 1;
+  p.kv_chunks = fa::xcd_chunks(Hkv);
+  p.scale_log2 = softmax_scale * kLog2eF;
+  p.tau = kDefaultTau;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.Nk = Nk;
+  p.q_off = Nk - Nq;
+  p.n_splits = n_splits;
+  p.chunk = (Nk + n_splits - 1) / n_splits;
+  hipError_t e = fa::fwd_split_launch(p, d, causal, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B, int H,
+                   int N, int d, void* stream) {
+  fa_status st = fa::check_merge(o_part, lse_part, o, lse, n_parts, B, H, N, d);
+  if (st != FA_OK) return st;
+  if (B == 0 || N == 0) return FA_OK;
+  hipError_t e = fa::merge_launch(o_part, lse_part, o, lse, n_parts, B, H, N, d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int varlen) {
   return fa::bwd_workspace_bytes(B, Hq, Hkv, N, d, causal, varlen);
 }

@@ -75,9 +75,12 @@ struct FwdStage {
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
+// SPLIT: partial results over one key chunk per work item (split-KV), written
+// as fp32 O_p and LSE_p; uniform batches only.
+template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(const FwdParams p) {
+  static_assert(!(SPLIT && VARLEN), "split-KV partial results are for uniform batches");
   using S = FwdStage<D>;
   using RC = RowCopy<D, BN>;
   constexpr int KSTEPS = D / 16;
@@ -103,24 +106,36 @@ void fa_fwd_kernel(const FwdParams p) {
   const int hl = lane >> 5, l32 = lane & 31;
 
   // ---- work item -> (sequence s, query head h, query tile qt), in the order
-  // fa_order.h describes ----
+  // fa_order.h describes; a split call's items are (sequence, chunk sp) pairs
+  // in place of sequences ----
   TileItem item;
   if constexpr (VARLEN) {
     if (!q_item_xcd(blockIdx.x, p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles, p.lpt, item)) return;
   } else {
-    if (!q_item_level(blockIdx.x, p.B, p.Hq, p.G, p.n_qtiles, p.lpt, item)) return;
+    if (!q_item_level(blockIdx.x, SPLIT ? p.B * p.n_splits : p.B, p.Hq, p.G, p.n_qtiles, p.lpt, item)) return;
   }
-  const int s = item.s, h = item.h, qt = item.t;
+  const int s = SPLIT ? item.s / p.n_splits : item.s;
+  const int sp = SPLIT ? item.s - s * p.n_splits : 0;
+  const int h = item.h, qt = item.t;
   const int hkv = h / p.G;
 
-  int seq0, L;
+  int seq0, L, kseq0, Lk;                           // queries: rows seq0.., L of them; keys: kseq0.., Lk
   if constexpr (VARLEN) {
     seq0 = p.cu_seqlens[s];
     L = p.cu_seqlens[s + 1] - seq0;
+    kseq0 = seq0;
+    Lk = L;
   } else {
     seq0 = s * p.N;
     L = p.N;
+    kseq0 = SPLIT ? s * p.Nk : seq0;
+    Lk = SPLIT ? p.Nk : L;
   }
+  // keys of this work item: [kb, ke), the chunk of a split call; query i sits
+  // at key position i + q_off for the causal mask
+  const int q_off = SPLIT ? p.q_off : 0;
+  const int kb = SPLIT ? min(sp * p.chunk, Lk) : 0;
+  const int ke = SPLIT ? (int)min((long)(sp + 1) * p.chunk, (long)Lk) : Lk;
   const int q0 = qt * BM;
   if (q0 >= L) return;
   const int qw0 = q0 + wave * WQ;                   // first query of this wave
@@ -130,10 +145,10 @@ void fa_fwd_kernel(const FwdParams p) {
 
   const long q_row_stride = (long)p.Hq * D;         // elements
   const long kv_stride = (long)p.Hkv * D * 2;       // bytes per token row of K/V
-  const char* kbase = (const char*)p.k + ((long)seq0 * p.Hkv + hkv) * D * 2;
-  const char* vbase = (const char*)p.v + ((long)seq0 * p.Hkv + hkv) * D * 2;
-  const int kv_end = CAUSAL ? min(L, q0 + BM) : L;  // keys this workgroup can see
-  const int n_it = (kv_end + BN - 1) / BN;
+  const char* kbase = (const char*)p.k + ((long)kseq0 * p.Hkv + hkv) * D * 2;
+  const char* vbase = (const char*)p.v + ((long)kseq0 * p.Hkv + hkv) * D * 2;
+  const int kv_end = CAUSAL ? min(ke, q0 + BM + q_off) : ke;   // keys this workgroup can see
+  const int n_it = kv_end > kb ? (kv_end - kb + BN - 1) / BN : 0;
 
   // ---- Q fragments (B operands of S^T = K Q^T): lane holds queries my_q[qb] ----
   bf16x8 qf[2][KSTEPS];
@@ -149,8 +164,8 @@ void fa_fwd_kernel(const FwdParams p) {
   copy.init(wave, lane, (unsigned)kv_stride);
   int iss = 0;
   auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
-    copy.issue(stage, kbase, kv_stride, iss * BN, L);
-    copy.issue(stage + S::TILEB, vbase, kv_stride, iss * BN, L);
+    copy.issue(stage, kbase, kv_stride, kb + iss * BN, ke);
+    copy.issue(stage + S::TILEB, vbase, kv_stride, kb + iss * BN, ke);
     ++iss;
   };
 
@@ -213,12 +228,12 @@ void fa_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool dead = (key >= L) || (CAUSAL && key > my_q[qb]);
+        const bool dead = (key >= ke) || (CAUSAL && key > my_q[qb] + q_off);
         if (dead) sx[qb][r] = -INFINITY;
       }
   };
   auto needs_mask = [&](int k0) __attribute__((always_inline)) {
-    return (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > qw0);
+    return (k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > qw0 + q_off);
   };
   float mpart[2];
   auto max_half = [&](const f32x16 (&sx)[2], int qb, int half) __attribute__((always_inline)) {
@@ -310,7 +325,7 @@ void fa_fwd_kernel(const FwdParams p) {
     barrier_no_fence();
     const bool issue = i + 3 < n_it;
     char FA_LDS* const nst = stage((BI + 3) % NSTAGE);
-    const int k_next = (i + 1) * BN;
+    const int k_next = kb + (i + 1) * BN;
     if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, k_next, issue, nst);
     else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, k_next, issue, nst);
   };
@@ -322,7 +337,20 @@ void fa_fwd_kernel(const FwdParams p) {
   // 2^tau, and the pass is exact. Otherwise the workgroup runs the loop again
   // with each row's true maximum, where no rescaling can be needed.
   __shared__ int over_flag[NWAVES];
-  for (int pass = 0;; ++pass) {
+  bool run = true;
+  if constexpr (SPLIT) {
+    if (n_it == 0) {                  // the chunk holds no key any query of the workgroup sees
+      run = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
+        l_run[qb] = 0.f;
+        m_run[qb] = -INFINITY;
+      }
+    }
+  }
+  for (int pass = 0; run; ++pass) {
     iss = 0;
     issue_next(stage(0));
     if (n_it > 1) issue_next(stage(1));
@@ -356,7 +384,7 @@ void fa_fwd_kernel(const FwdParams p) {
       }
     }
     mfma_result_wait();
-    if (needs_mask(0)) mask_tile(sA, 0);
+    if (needs_mask(kb)) mask_tile(sA, kb);
     max_half(sA, 0, 0);
     max_half(sA, 0, 1);
     max_half(sA, 1, 0);
@@ -393,6 +421,24 @@ void fa_fwd_kernel(const FwdParams p) {
   }
 
   // ---- epilogue: O = O / l, LSE = m * scale + ln(l) ----
+  if constexpr (SPLIT) {
+    // fp32 O_p rows straight from the accumulators; rows that saw no key of
+    // the chunk hold O_p = 0, LSE_p = -inf
+    const long part = (long)sp * p.B + s;
+    float* ob = p.o_part + (part * p.N * p.Hq + h) * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l_tot = pair_sum(l_run[qb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      store_rows_f32<D>(oacc[qb], inv, ob, q_row_stride, qw0 + 32 * qb, L, lane);
+      if (hl == 0 && my_q[qb] < L) {
+        const float lse = (m_run[qb] == -INFINITY || l_tot == 0.f) ? -INFINITY
+                                                                  : (m_run[qb] * c + __log2f(l_tot)) * kLn2;
+        p.lse_part[(part * p.Hq + h) * p.N + my_q[qb]] = lse;
+      }
+    }
+    return;
+  }
   barrier_no_fence();
   char FA_LDS* st = stage(0);
   if (wave == 1) st = stage(1);
@@ -422,7 +468,14 @@ void fa_fwd_kernel(const FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
 static hipError_t launch_fwd(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, EXPMODE>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, EXPMODE, false>), dim3(grid), dim3(NTHREADS), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_split(const FwdParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false, 0, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -452,6 +505,16 @@ hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, h
   const int grid = (int)grid_l;
   if (d == 128) return launch_fwd_d<128>(p, grid, causal, varlen, expmode, stream);
   return launch_fwd_d<64>(p, grid, causal, varlen, expmode, stream);
+}
+
+hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream) {
+  p.n_qtiles = (p.N + BM - 1) / BM;
+  const long grid_l = q_grid_level(p.B * p.n_splits, p.Hq, p.G, p.n_qtiles);
+  if (grid_l == 0) return hipSuccess;
+  if (grid_l > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const int grid = (int)grid_l;
+  if (d == 128) return causal ? launch_split<128, true>(p, grid, stream) : launch_split<128, false>(p, grid, stream);
+  return causal ? launch_split<64, true>(p, grid, stream) : launch_split<64, false>(p, grid, stream);
 }
 
 }  // namespace fa

@@ -19,9 +19,19 @@ struct FwdParams {
   int lpt;                     // 1: heaviest query tiles first
   float scale_log2;            // softmax_scale * log2(e)
   float tau;                   // conditional rescale threshold (log2 units)
+  // split-KV partial results (fwd_split_launch); N is then the number of queries
+  float* o_part;               // fp32 [n_splits, B, N, Hq, d]
+  float* lse_part;             // fp32 [n_splits, B, Hq, N]
+  int Nk;                      // keys per sequence
+  int q_off;                   // Nk - N: key position of query 0
+  int n_splits;
+  int chunk;                   // keys per chunk, ceil(Nk / n_splits)
 };
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream);
+hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream);
+hipError_t merge_launch(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B,
+                        int H, int N, int d, hipStream_t stream);
 int fwd_block_m();
 
 struct BwdParams {

@@ -121,6 +121,26 @@ __device__ __forceinline__ void store_rows_bf16(char FA_LDS* st, const f32x16* a
   }
 }
 
+// Rows row0 + l32 (lanes l32 and l32 + 32) of a wave's fp32 accumulators, times
+// `mul`, written straight to global memory: lane (l32, hl) holds columns
+// db*32 + 8(r/4) + 4 hl + r%4 of its row, four consecutive floats per 16-byte store.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const f32x16* acc, float mul, float* gbase, long row_stride,
+                                               int row0, int L, int lane) {
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int r = row0 + l32;
+  if (r >= L) return;
+  float* rowp = gbase + (long)r * row_stride;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = {acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul, acc[db][4 * g + 2] * mul,
+                       acc[db][4 * g + 3] * mul};
+      *(f32x4*)(rowp + db * 32 + 8 * g + 4 * hl) = v;
+    }
+}
+
 // Wait until at most `n` vector-memory operations of this wave are outstanding
 // and no LDS operation is (n must be a compile-time constant after inlining;
 // values above 20 wait for everything).

@@ -76,4 +76,35 @@ inline fa_status check_bwd(const void* q, const void* k, const void* v, const vo
   return FA_OK;
 }
 
+constexpr long kMaxSplits = 1024;
+
+inline fa_status check_split(const void* q, const void* k, const void* v, const float* o_part,
+                             const float* lse_part, long B, long Hq, long Hkv, long Nq, long Nk, long d,
+                             int causal, float scale, long n_splits) {
+  if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_INVALID_ARGUMENT;
+  if (Nk < 0 || Nq < 0) return FA_ERR_INVALID_ARGUMENT;
+  if (causal == 1 && Nq > Nk) return FA_ERR_INVALID_ARGUMENT;
+  const Problem pr{B, Hq, Hkv, Nq > Nk ? Nq : Nk, d, causal, 0};
+  fa_status st = check_problem(pr, scale);
+  if (st != FA_OK) return st;
+  if (B * Hq * ((Nq + 127) / 128) * n_splits > kMaxItems) return FA_ERR_UNSUPPORTED;
+  if (B * n_splits * Nq * Hq * d > (1L << 40)) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || !aligned4(lse_part))
+    return FA_ERR_INVALID_ARGUMENT;
+  return FA_OK;
+}
+
+inline fa_status check_merge(const float* o_part, const float* lse_part, const void* o, const float* lse,
+                             long n_parts, long B, long H, long N, long d) {
+  if (n_parts < 1 || n_parts > kMaxSplits || B < 0 || H <= 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B * N * H > kMaxTokens) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return FA_OK;
+  if (!o_part || !lse_part || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(o_part) || !aligned16(o) || !aligned4(lse_part) || !aligned4(lse)) return FA_ERR_INVALID_ARGUMENT;
+  return FA_OK;
+}
+
 }  // namespace fa

@@ -76,6 +76,8 @@ class Workload:
     varlen: bool = False
     len_lo: int = 0      # packed: inclusive length range of the uniform draw
     len_hi: int = 0
+    Nk: int = 0          # split-KV: keys per sequence (N is then the number of queries)
+    n_splits: int = 0    # split-KV: key chunks
 
     @property
     def scale(self) -> float:
@@ -101,6 +103,11 @@ WORKLOADS = {
     "bwd_causal_varlen16_hq32_hkv8_d128": Workload(
         "bwd_causal_varlen16_hq32_hkv8_d128", "bwd", Hq=32, Hkv=8, d=128, causal=True, seed=4,
         B=16, varlen=True, len_lo=512, len_hi=16384),
+    # split-KV partial results + merge: 512 queries (the last 512 positions)
+    # against 131072 keys, 16 key chunks
+    "split_causal_b1_hq32_hkv8_nq512_nk131072_d128": Workload(
+        "split_causal_b1_hq32_hkv8_nq512_nk131072_d128", "split", Hq=32, Hkv=8, d=128, causal=True, seed=8,
+        B=1, N=512, Nk=131072, n_splits=16),
     # long context on one GPU
     "fwd_causal_b1_h16_n131072_d128": Workload(
         "fwd_causal_b1_h16_n131072_d128", "fwd", Hq=16, Hkv=16, d=128, causal=True, seed=6, B=1, N=131072),
@@ -177,8 +184,47 @@ def make_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, causal: bool, seed: i
                   causal=causal, scale=scale)
 
 
+@dataclasses.dataclass
+class SplitInputs:
+    """bf16 bit patterns of a split-KV problem: Q [B, Nq, Hq, d], K/V [B, Nk, Hkv, d]."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    B: int
+    Nq: int
+    Nk: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    scale: float
+    n_splits: int
+
+
+def make_split_inputs(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, causal: bool, seed: int,
+                      n_splits: int, scale: Optional[float] = None) -> SplitInputs:
+    """Q, K, V drawn in that order, as for the other workloads."""
+    rng = np.random.default_rng(seed)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = _draw_bf16(rng, (B, Nq, Hq, d))
+    k = _draw_bf16(rng, (B, Nk, Hkv, d))
+    v = _draw_bf16(rng, (B, Nk, Hkv, d))
+    return SplitInputs(q=q, k=k, v=v, B=B, Nq=Nq, Nk=Nk, Hq=Hq, Hkv=Hkv, d=d, causal=causal, scale=scale,
+                       n_splits=n_splits)
+
+
+def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
+    """(query, key) pairs a split-KV problem computes: query i sees keys <= i + Nk - Nq when causal."""
+    if not causal:
+        return Nq * Nk
+    return Nq * (Nk - Nq) + Nq * (Nq + 1) // 2
+
+
 def workload_inputs(name: str) -> Inputs:
     w = WORKLOADS[name]
+    if w.kind == "split":
+        return make_split_inputs(w.B, w.N, w.Nk, w.Hq, w.Hkv, w.d, w.causal, w.seed, w.n_splits, scale=w.scale)
     if w.varlen:
         return make_inputs(w.B, 0, w.Hq, w.Hkv, w.d, w.causal, w.seed, scale=w.scale,
                            with_do=(w.kind == "bwd"), len_range=(w.len_lo, w.len_hi), n_seqs=w.B)

@@ -74,3 +74,43 @@ def backward(q, k, v, o, lse, do, causal: bool, scale: Optional[float] = None, c
     capi.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens,
                 workspace, workspace.numel(), stream)
     return dq, dk, dv
+
+
+def forward_split(q, k, v, causal: bool, n_splits: int, scale: Optional[float] = None, stream=None,
+                  o_part=None, lse_part=None):
+    """Split-KV partial results of uniform batches: Q [B, Nq, Hq, d], K/V [B, Nk, Hkv, d].
+
+    Returns (O_part fp32 [n, B, Nq, Hq, d], LSE_part fp32 [n, B, Hq, Nq]).
+    """
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check(n, t)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("split-KV takes uniform [B, N, H, d] tensors")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("K/V shape does not match Q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o_part is None:
+        o_part = torch.empty((n_splits, B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, B, Hq, Nq), dtype=torch.float32, device=q.device)
+    capi.fa_fwd_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, int(causal), scale, n_splits, stream)
+    return o_part, lse_part
+
+
+def merge(o_part, lse_part, stream=None, out=None, lse=None):
+    """Merge partial results O_part [n, B, N, H, d], LSE_part [n, B, H, N] (fp32) -> (O bf16, LSE fp32)."""
+    _check("o_part", o_part, torch.float32)
+    _check("lse_part", lse_part, torch.float32)
+    if o_part.dim() != 5 or lse_part.dim() != 4:
+        raise ValueError("partials are O [n, B, N, H, d] and LSE [n, B, H, N]")
+    n, B, N, H, d = o_part.shape
+    if tuple(lse_part.shape) != (n, B, H, N):
+        raise ValueError("LSE partials do not match the O partials")
+    o = out if out is not None else torch.empty((B, N, H, d), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
+    capi.fa_merge(o_part, lse_part, o, lse, n, B, H, N, d, stream)
+    return o, lse

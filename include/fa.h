@@ -149,6 +149,50 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, int stages,
                     void* stream);
 
+/*
+ * Split-KV partial attention (uniform batches). The keys of every sequence are
+ * cut into n_splits contiguous chunks of C = ceil(Nk / n_splits) keys (chunk p:
+ * keys p*C .. min((p+1)*C, Nk) - 1; chunks past the end are empty). For every
+ * query i and chunk p it writes the attention over that chunk's keys alone:
+ *   LSE_p(i) = ln sum_{j in chunk p, visible} exp(scale * q_i . k_j)
+ *   O_p(i)   = sum_{j in chunk p, visible} exp(scale * q_i . k_j - LSE_p(i)) v_j
+ * and LSE_p(i) = -inf, O_p(i) = 0 where query i sees no key of the chunk.
+ * fa_merge of the parts gives the attention over all keys. This is the
+ * combination step of the online softmax applied across key chunks
+ * (podcast.app episode page, description; Ring Attention in its source list),
+ * for long key ranges with few queries (decoding, chunked prefill) and for the
+ * per-chunk results of sequence-parallel attention.
+ *   q         bf16 [B, Nq, Hq, d]
+ *   k, v      bf16 [B, Nk, Hkv, d]
+ *   o_part    fp32 [n_splits, B, Nq, Hq, d]   device memory owned by the caller
+ *   lse_part  fp32 [n_splits, B, Hq, Nq]      device memory owned by the caller
+ *   causal    query i sits at key position i + Nk - Nq (the last query sees
+ *             every key); requires Nq <= Nk
+ *   n_splits  1 .. 1024
+ * Other arguments as for fa_fwd. Returns FA_ERR_INVALID_ARGUMENT for bad
+ * sizes, flags or pointers, FA_ERR_UNSUPPORTED for other head sizes.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                       int n_splits, void* stream);
+
+/*
+ * Merge of partial attention results (the combination step of the online
+ * softmax, podcast.app episode page, description), row by row:
+ *   LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
+ * Rows whose every part has LSE_p = -inf get LSE = -inf and O = 0.
+ *   o_part    fp32 [n_parts, B, N, H, d]   (fa_fwd_split's layout, any producer)
+ *   lse_part  fp32 [n_parts, B, H, N]
+ *   o         bf16 [B, N, H, d] (output)
+ *   lse       fp32 [B, H, N]    (output)
+ * A packed [T, H, d] / [H, T] pair is B = 1, N = T. d in {64, 128},
+ * n_parts 1 .. 1024. Device pointers, caller-owned; o_part and o, or lse_part
+ * and lse, must not overlap. Returns FA_ERR_INVALID_ARGUMENT for bad sizes or
+ * pointers, FA_ERR_UNSUPPORTED for other d.
+ */
+fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                   int n_parts, int B, int H, int N, int d, void* stream);
+
 /* Static, human-readable description of a status code. */
 const char* fa_status_string(fa_status s);
 

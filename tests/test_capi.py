@@ -110,3 +110,46 @@ def test_workspace_size(lib):
     assert capi.fa_bwd_workspace_size(2, 16, 16, 8192, 128, 1, 0) == 2 * (2 * 8192 * 16 * 4)
     n = capi.fa_bwd_workspace_size(3, 5, 5, 7, 64, 0, 1)
     assert n >= 2 * 3 * 7 * 5 * 4 and n % 256 == 0
+
+
+def split(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, Nq=16, Nk=64, d=128, causal=1, scale=0.1, n=4):
+    return capi.fa_fwd_split(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, n, stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(n=1025), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(Nq=65, Nk=64), capi.FA_ERR_INVALID_ARGUMENT),       # causal needs Nq <= Nk
+    (dict(Nk=-1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), capi.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=A + 4), capi.FA_ERR_INVALID_ARGUMENT),            # fp32 partial rows need 16-byte alignment
+    (dict(causal=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), capi.FA_OK),                                   # empty: nothing to do
+    (dict(Nq=0), capi.FA_OK),
+])
+def test_split_rejects(lib, kw, expect):
+    assert split(**kw) == expect
+
+
+def merge(*, op=A, lp=A, o=A, lse=A, n=2, B=1, H=2, N=16, d=128):
+    return capi.fa_merge(op, lp, o, lse, n, B, H, N, d, stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(n=0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(n=1025), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), capi.FA_ERR_UNSUPPORTED),
+    (dict(op=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(lse=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), capi.FA_OK),
+    (dict(N=0), capi.FA_OK),
+])
+def test_merge_rejects(lib, kw, expect):
+    assert merge(**kw) == expect
