@@ -28,6 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz (AMD: "2.5 PFLOP/s" dense BF16)
+PEAK_FP8_TFLOPS = 5033.2      # dense 8-bit MFMA, twice the bf16 rate (AMD: "5.0 PFLOP/s")
+# the 8-bit Q/K forward runs half its counted work (Q K^T) at the 8-bit rate and half (P V) at the bf16 rate
+PEAK_QK8_PV16_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X (% of dense BF16 MFMA peak)"
 MAIN = "fwd_b4_h16_n4096_d128"
@@ -246,6 +249,28 @@ def main():
                 del dow, dqw, dkw, dvw, wsw
             workloads[name] = ent
             del qw, kw, vw, ow, lse_w
+            torch.cuda.empty_cache()
+
+        # 8-bit Q/K forward: E4M3 codes drawn as N(0, 64^2) rounded by PyTorch's float8_e4m3fn
+        # conversion (|x| < 448 at these sizes), descale 1/64 for every (sequence, head)
+        for name in ("fp8_fwd_b4_h16_n4096_d128", "fp8_fwd_causal_b2_h16_n16384_d128"):
+            wl = I.WORKLOADS[name]
+            qs, ks = (wl.B, wl.N, wl.Hq, wl.d), (wl.B, wl.N, wl.Hkv, wl.d)
+            q8 = (rnd(qs, wl.seed * 10 + 1).float() * 64).to(torch.float8_e4m3fn).view(torch.uint8)
+            k8 = (rnd(ks, wl.seed * 10 + 2).float() * 64).to(torch.float8_e4m3fn).view(torch.uint8)
+            vw = rnd(ks, wl.seed * 10 + 3)
+            qd = torch.full((wl.B, wl.Hq), 1.0 / 64, dtype=torch.float32, device=dev)
+            kd = torch.full((wl.B, wl.Hkv), 1.0 / 64, dtype=torch.float32, device=dev)
+            ow = torch.empty(qs, dtype=torch.bfloat16, device=dev)
+            lw = torch.empty((wl.B, wl.Hq, wl.N), dtype=torch.float32, device=dev)
+            f8 = lambda: capi.fa_fwd_fp8(q8, k8, vw, qd, kd, ow, lw, wl.B, wl.Hq, wl.Hkv, wl.N, wl.d,
+                                         int(wl.causal), wl.scale, None, stream)
+            ms = time_it(f8, 5 if wl.N >= 8192 else 20)
+            fl = I.counted_flops(np.full(wl.B, wl.N), wl.Hq, wl.d, wl.causal)
+            workloads[name] = {"fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                               "fwd_frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "fwd_frac_of_qk8_pv16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_QK8_PV16_TFLOPS, 4)}
+            del q8, k8, vw, qd, kd, ow, lw
             torch.cuda.empty_cache()
 
         # split-KV partial results + merge: 512 queries against 131072 keys

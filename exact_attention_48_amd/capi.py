@@ -28,7 +28,8 @@ FA_BWD_DKDV = 2
 FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_split", "fa_merge",
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_split",
+            "fa_merge",
             "fa_status_string", "fa_version")
 
 
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = ci
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
     lib.fa_bwd_ex.restype = ci
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp]
+    lib.fa_fwd_fp8.restype = ci
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.fa_fwd_split.restype = ci
     lib.fa_merge.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
@@ -164,4 +167,13 @@ def fa_merge(o_part, lse_part, o, lse, n_parts: int, B: int, H: int, N: int, d: 
                          _stream(stream))
     if check and st != FA_OK:
         raise FaError(st, "fa_merge")
+    return st
+
+
+def fa_fwd_fp8(q8, k8, v, q_descale, k_descale, o, lse, B: int, Hq: int, Hkv: int, N: int, d: int, causal: int,
+               softmax_scale: float, cu_seqlens=None, stream=None, check: bool = True) -> int:
+    st = load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(o), _ptr(lse), B,
+                           Hq, Hkv, N, d, int(causal), float(softmax_scale), _ptr(cu_seqlens), _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
     return st

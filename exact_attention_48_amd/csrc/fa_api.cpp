@@ -93,6 +93,35 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, nullptr, stream);
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                     const int32_t* cu_seqlens, void* stream) {
+  const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
+  fa_status st = fa::check_fp8(q, k, v, q_descale, k_descale, o, lse, pr, softmax_scale, cu_seqlens);
+  if (st != FA_OK) return st;
+  if (fa::empty_problem(pr)) return FA_OK;
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.N = N;
+  p.lpt = 1;
+  p.kv_chunks = fa::xcd_chunks(Hkv);
+  p.scale_log2 = softmax_scale * kLog2eF;
+  p.tau = kDefaultTau;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  hipError_t e = fa::fwd_fp8_launch(p, causal, cu_seqlens != nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                        int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
                        int n_splits, void* stream) {

@@ -22,6 +22,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -52,6 +54,14 @@ __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x
 //   acc (AGPR) += A * B, A and B in VGPRs
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 8-bit MFMA: S^T (VGPR accumulator) from K (A, VGPRs) and Q^T (B, AGPRs), both
+// OCP E4M3 (format fields 0), 32 bytes of the contraction per lane and operand.
+__device__ __forceinline__ void mfma8_v_first(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma8_v(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
 // acc *= alpha for an accumulator held in AGPRs, in place (each register read
 // to a VGPR, multiplied, written back), so that the compiler never moves the

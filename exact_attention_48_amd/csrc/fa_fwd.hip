@@ -64,11 +64,13 @@ constexpr int WQ = 64;               // queries per wave
 constexpr int BM = NWAVES * WQ;      // queries per workgroup
 constexpr int BN = 32;               // keys per K/V tile
 
-template <int D>
+// One ring stage: a K tile (bf16, or 8-bit when K8) and a bf16 V tile.
+template <int D, bool K8>
 struct FwdStage {
   static constexpr int ROWB = D * 2;
-  static constexpr int TILEB = BN * ROWB;           // one K or V tile
-  static constexpr int BYTES = 2 * TILEB;
+  static constexpr int KTILEB = BN * (K8 ? D : ROWB);
+  static constexpr int VOFF = KTILEB;               // V tile offset
+  static constexpr int BYTES = KTILEB + BN * ROWB;
   static constexpr int OROWB = ROWB + 16;           // output staging pitch
   static_assert(32 * OROWB <= BYTES, "32 rows of a wave's output staging must fit in one stage");
 };
@@ -77,15 +79,20 @@ struct FwdStage {
 
 // SPLIT: partial results over one key chunk per work item (split-KV), written
 // as fp32 O_p and LSE_p; uniform batches only.
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT>
+// FP8: Q and K as OCP E4M3 codes with per-(sequence, head) descales; S^T by the
+// 32x32x64 8-bit MFMA (64 of the contraction per instruction), V and P bf16.
+template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(const FwdParams p) {
   static_assert(!(SPLIT && VARLEN), "split-KV partial results are for uniform batches");
-  using S = FwdStage<D>;
-  using RC = RowCopy<D, BN>;
-  constexpr int KSTEPS = D / 16;
+  static_assert(!(SPLIT && FP8) && (!FP8 || D == 128), "8-bit Q/K: plain forward, d = 128");
+  using S = FwdStage<D, FP8>;
+  using RCK = RowCopy<FP8 ? D / 2 : D, BN>;         // an 8-bit row of D bytes copies like a bf16 row of D / 2
+  using RCV = RowCopy<D, BN>;
+  constexpr int KSTEPS = FP8 ? D / 64 : D / 16;      // S^T k-steps
   constexpr int DBLK = D / 32;
-  constexpr int OPS = 2 * RC::PER_WAVE;             // copy instructions per tile and wave
+  constexpr int OPS = RCK::PER_WAVE + RCV::PER_WAVE; // copy instructions per tile and wave
+  using AFrag = std::conditional_t<FP8, i32x8, bf16x8>;
   __shared__ __attribute__((aligned(1024))) char s0_raw[S::BYTES];
   __shared__ __attribute__((aligned(1024))) char s1_raw[S::BYTES];
   __shared__ __attribute__((aligned(1024))) char s2_raw[S::BYTES];
@@ -144,34 +151,53 @@ void fa_fwd_kernel(const FwdParams p) {
   my_q[1] = qw0 + 32 + l32;
 
   const long q_row_stride = (long)p.Hq * D;         // elements
-  const long kv_stride = (long)p.Hkv * D * 2;       // bytes per token row of K/V
-  const char* kbase = (const char*)p.k + ((long)kseq0 * p.Hkv + hkv) * D * 2;
+  const long kv_stride = (long)p.Hkv * D * 2;       // bytes per token row of V (and of bf16 K)
+  const long k_stride = FP8 ? (long)p.Hkv * D : kv_stride;
+  const char* kbase = (const char*)p.k + ((long)kseq0 * p.Hkv + hkv) * D * (FP8 ? 1 : 2);
   const char* vbase = (const char*)p.v + ((long)kseq0 * p.Hkv + hkv) * D * 2;
   const int kv_end = CAUSAL ? min(ke, q0 + BM + q_off) : ke;   // keys this workgroup can see
   const int n_it = kv_end > kb ? (kv_end - kb + BN - 1) / BN : 0;
 
-  // ---- Q fragments (B operands of S^T = K Q^T): lane holds queries my_q[qb] ----
-  bf16x8 qf[2][KSTEPS];
+  // ---- Q fragments (B operands of S^T = K Q^T): lane holds queries my_q[qb];
+  // bf16: elements 16 ks + 8 hl .. + 7; 8-bit: bytes 64 ks + 32 hl .. + 31 ----
+  AFrag qf[2][KSTEPS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qr = my_q[qb] < L ? my_q[qb] : L - 1;
-    const __bf16* qp = (const __bf16*)p.q + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 8;
+    if constexpr (FP8) {
+      const char* qp = (const char*)p.q + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 32;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const i32x4 lo = *(const i32x4*)(qp + ks * 64);
+        const i32x4 hi = *(const i32x4*)(qp + ks * 64 + 16);
+        qf[qb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    } else {
+      const __bf16* qp = (const __bf16*)p.q + ((long)(seq0 + qr) * p.Hq + h) * D + hl * 8;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) qf[qb][ks] = *(const bf16x8*)(qp + ks * 16);
+    }
   }
 
-  RC copy;
-  copy.init(wave, lane, (unsigned)kv_stride);
+  RCK kcopy;
+  RCV vcopy;
+  kcopy.init(wave, lane, (unsigned)k_stride);
+  vcopy.init(wave, lane, (unsigned)kv_stride);
   int iss = 0;
   auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
-    copy.issue(stage, kbase, kv_stride, kb + iss * BN, ke);
-    copy.issue(stage + S::TILEB, vbase, kv_stride, kb + iss * BN, ke);
+    kcopy.issue(stage, kbase, k_stride, kb + iss * BN, ke);
+    vcopy.issue(stage + S::VOFF, vbase, kv_stride, kb + iss * BN, ke);
     ++iss;
   };
 
   TileOffsets<D> to;
   to.init(lane);
-  const float c = p.scale_log2;
+  TileOffsetsK8 to8;
+  if constexpr (FP8) to8.init(lane);
+  // exp2 argument scale: softmax_scale * log2(e), times the Q and K descales of
+  // this (sequence, head) for 8-bit inputs
+  float c = p.scale_log2;
+  if constexpr (FP8) c = c * p.q_descale[(long)s * p.Hq + h] * p.k_descale[(long)s * p.Hkv + hkv];
   const float tau = p.tau;
   f32x16 oacc[2][DBLK];
   float m_run[2];                            // the max O and l are relative to (fixed in a pass)
@@ -185,18 +211,26 @@ void fa_fwd_kernel(const FwdParams p) {
   // S^T MFMA j: k-step j / 2, query block j % 2; the K fragment of a k-step is
   // read once for both blocks.
   constexpr int NA = 2 * KSTEPS;
-  auto a_frag = [&](const char FA_LDS* tile, int ks) __attribute__((always_inline)) {
-    return to.row_operand(tile, ks, 0);
+  auto a_frag = [&](const char FA_LDS* tile, int ks) __attribute__((always_inline)) -> AFrag {
+    if constexpr (FP8) return to8.operand(tile, ks);
+    else return to.row_operand(tile, ks, 0);
   };
-  auto a_step = [&](f32x16 (&sx)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
+  auto a_step = [&](f32x16 (&sx)[2], int j, const AFrag& a) __attribute__((always_inline)) {
     const int ks = j >> 1, qb = j & 1;
-    if (ks == 0) mfma_v_first(sx[qb], a, qf[qb][ks]);
-    else mfma_v(sx[qb], a, qf[qb][ks]);
+    if constexpr (FP8) {
+      if (ks == 0) mfma8_v_first(sx[qb], a, qf[qb][ks]);
+      else mfma8_v(sx[qb], a, qf[qb][ks]);
+    } else {
+      if (ks == 0) mfma_v_first(sx[qb], a, qf[qb][ks]);
+      else mfma_v(sx[qb], a, qf[qb][ks]);
+    }
   };
+  // K fragments read ahead in phase A (at most one per k-step)
+  constexpr int PFA = PF < KSTEPS ? PF : KSTEPS;
   // V^T fragment f: key step t = f / DBLK, d-block db = f % DBLK (both query blocks)
   constexpr int NV = 2 * DBLK;
   auto v_frag = [&](const char FA_LDS* tile, int f) __attribute__((always_inline)) {
-    return to.tr_operand(tile + S::TILEB, f / DBLK, f % DBLK);
+    return to.tr_operand(tile + S::VOFF, f / DBLK, f % DBLK);
   };
 
   // ---- softmax pieces ----
@@ -257,21 +291,21 @@ void fa_fwd_kernel(const FwdParams p) {
   //   phase B2: masking / maxima / decisions of the next tile (S^T in sx)
   constexpr int UA = 24;
   constexpr int UB = 34 - UA;
-  constexpr int VPRE = (PF < NV) ? PF : NV;         // V^T fragments read during phase A
+  constexpr int VPRE = (PFA < NV) ? PFA : NV;       // V^T fragments read during phase A
   auto stream = [&](const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2], const f32x16 (&sc)[2],
                     int k_next, bool issue, char FA_LDS* issue_stage) __attribute__((always_inline)) {
-    bf16x8 qa[PF];
+    AFrag qa[PFA];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) qa[i] = a_frag(nt, i);
+    for (int i = 0; i < PFA; ++i) qa[i] = a_frag(nt, i);
     if (issue) issue_next(issue_stage);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 vf[NV];                                  // V^T fragments, kept for both query blocks
     // phase A: S^T of the next tile; fragment ks feeds MFMAs 2 ks and 2 ks + 1
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const bf16x8 a = qa[ks % PF];
-      if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(nt, ks + PF);
-      else if (ks + PF - KSTEPS < VPRE) vf[ks + PF - KSTEPS] = v_frag(ct, ks + PF - KSTEPS);
+      const AFrag a = qa[ks % PFA];
+      if (ks + PFA < KSTEPS) qa[ks % PFA] = a_frag(nt, ks + PFA);
+      else if (ks + PFA - KSTEPS < VPRE) vf[ks + PFA - KSTEPS] = v_frag(ct, ks + PFA - KSTEPS);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int j = 2 * ks + x;
@@ -371,13 +405,13 @@ void fa_fwd_kernel(const FwdParams p) {
     else wait_vm(0);
     barrier_no_fence();
     {
-      bf16x8 qa[PF];
+      AFrag qa[PFA];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) qa[i] = a_frag(stage(0), i);
+      for (int i = 0; i < PFA; ++i) qa[i] = a_frag(stage(0), i);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 a = qa[ks % PF];
-        if (ks + PF < KSTEPS) qa[ks % PF] = a_frag(stage(0), ks + PF);
+        const AFrag a = qa[ks % PFA];
+        if (ks + PFA < KSTEPS) qa[ks % PFA] = a_frag(stage(0), ks + PFA);
         a_step(sA, 2 * ks, a);
         a_step(sA, 2 * ks + 1, a);
         __builtin_amdgcn_sched_barrier(0);
@@ -468,14 +502,21 @@ void fa_fwd_kernel(const FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN, int EXPMODE>
 static hipError_t launch_fwd(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, EXPMODE, false>), dim3(grid), dim3(NTHREADS), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, EXPMODE, false, false>), dim3(grid), dim3(NTHREADS), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_split(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false, 0, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, false, 0, true, false>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool CAUSAL, bool VARLEN>
+static hipError_t launch_fp8(const FwdParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<128, CAUSAL, VARLEN, 0, false, true>), dim3(grid), dim3(NTHREADS), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
@@ -515,6 +556,17 @@ hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream) 
   const int grid = (int)grid_l;
   if (d == 128) return causal ? launch_split<128, true>(p, grid, stream) : launch_split<128, false>(p, grid, stream);
   return causal ? launch_split<64, true>(p, grid, stream) : launch_split<64, false>(p, grid, stream);
+}
+
+hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, hipStream_t stream) {
+  p.n_qtiles = (p.N + BM - 1) / BM;
+  const long grid_l = varlen ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles)
+                             : q_grid_level(p.B, p.Hq, p.G, p.n_qtiles);
+  if (grid_l == 0) return hipSuccess;
+  if (grid_l > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const int grid = (int)grid_l;
+  if (causal) return varlen ? launch_fp8<true, true>(p, grid, stream) : launch_fp8<true, false>(p, grid, stream);
+  return varlen ? launch_fp8<false, true>(p, grid, stream) : launch_fp8<false, false>(p, grid, stream);
 }
 
 }  // namespace fa

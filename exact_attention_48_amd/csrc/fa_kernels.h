@@ -26,10 +26,14 @@ struct FwdParams {
   int q_off;                   // Nk - N: key position of query 0
   int n_splits;
   int chunk;                   // keys per chunk, ceil(Nk / n_splits)
+  // 8-bit Q/K (fwd_fp8_launch): q and k hold E4M3 codes, dequantised by these
+  const float* q_descale;      // [B, Hq]
+  const float* k_descale;      // [B, Hkv]
 };
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream);
 hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream);
+hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, hipStream_t stream);
 hipError_t merge_launch(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B,
                         int H, int N, int d, hipStream_t stream);
 int fwd_block_m();

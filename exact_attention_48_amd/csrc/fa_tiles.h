@@ -91,6 +91,26 @@ struct TileOffsets {
   }
 };
 
+// Per-lane LDS offsets of the 8-bit K operand of the 32x32x64 MFMA in a tile of
+// 128-byte rows (E4M3, d = 128), swizzled like a bf16 [rows][64] tile. Lane
+// (row l32, half hl) takes bytes 64 ks + 32 hl .. + 31 of its row for k-step ks:
+// logical 16-byte chunks 4 ks + 2 hl and 4 ks + 2 hl + 1. The Q^T operand holds
+// the same bytes of the query rows, so the contraction pairs them up.
+struct TileOffsetsK8 {
+  int off[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int hl = lane >> 5, l32 = lane & 31;
+    const int sw = lds_swz<64>(l32);
+    off[0] = l32 * 128 + (((2 * hl) ^ sw) << 4);
+    off[1] = l32 * 128 + (((2 * hl + 1) ^ sw) << 4);
+  }
+  __device__ __forceinline__ i32x8 operand(const char FA_LDS* tile, int ks) const {
+    const i32x4 lo = __builtin_bit_cast(i32x4, lds_read16(tile + (off[0] ^ (ks << 6))));
+    const i32x4 hi = __builtin_bit_cast(i32x4, lds_read16(tile + (off[1] ^ (ks << 6))));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // Stage a wave's 32 x D fp32 accumulator (transposed C layout: lane = row
 // l32, register r of block db = column db*32 + 8(r/4) + 4(l/32) + r%4) as bf16
 // through LDS and write whole 16-byte row segments to global memory.

@@ -76,6 +76,17 @@ inline fa_status check_bwd(const void* q, const void* k, const void* v, const vo
   return FA_OK;
 }
 
+inline fa_status check_fp8(const void* q, const void* k, const void* v, const float* qd, const float* kd,
+                           const void* o, const float* lse, const Problem& pr, float scale,
+                           const int32_t* cu_seqlens) {
+  fa_status st = check_fwd(q, k, v, o, lse, pr, scale, cu_seqlens, nullptr);
+  if (st != FA_OK) return st;
+  if (pr.d != 128) return FA_ERR_UNSUPPORTED;
+  if (empty_problem(pr)) return FA_OK;
+  if (!qd || !kd || !aligned4(qd) || !aligned4(kd)) return FA_ERR_INVALID_ARGUMENT;
+  return FA_OK;
+}
+
 constexpr long kMaxSplits = 1024;
 
 inline fa_status check_split(const void* q, const void* k, const void* v, const float* o_part,

@@ -59,13 +59,43 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# OCP E4M3 encoding of inputs (round to nearest, ties to even, saturating)
+# --------------------------------------------------------------------------
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite E4M3 values, indexed by code 0x00..0x7E."""
+    m = np.arange(8, dtype=np.float64)
+    vals = [m / 8.0 * 2.0 ** -6]
+    for e in range(1, 16):
+        vals.append((1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.concatenate(vals)[:0x7F]
+
+
+_E4M3 = _e4m3_magnitudes()
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float values to OCP E4M3 (nearest, ties to the even code; magnitudes
+    above 448 saturate to 448), returning uint8 codes. NaN maps to 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), _E4M3[-1])
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - _E4M3[lo], _E4M3[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x) & (code != 0), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
 # Workload descriptions
 # --------------------------------------------------------------------------
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "fwd" or "bwd"
+    kind: str            # "fwd", "bwd", "split" or "fp8"
     Hq: int
     Hkv: int
     d: int
@@ -108,6 +138,11 @@ WORKLOADS = {
     "split_causal_b1_hq32_hkv8_nq512_nk131072_d128": Workload(
         "split_causal_b1_hq32_hkv8_nq512_nk131072_d128", "split", Hq=32, Hkv=8, d=128, causal=True, seed=8,
         B=1, N=512, Nk=131072, n_splits=16),
+    # 8-bit Q/K forward (E4M3, per-(sequence, head) descales), non-causal and causal
+    "fp8_fwd_b4_h16_n4096_d128": Workload(
+        "fp8_fwd_b4_h16_n4096_d128", "fp8", Hq=16, Hkv=16, d=128, causal=False, seed=9, B=4, N=4096),
+    "fp8_fwd_causal_b2_h16_n16384_d128": Workload(
+        "fp8_fwd_causal_b2_h16_n16384_d128", "fp8", Hq=16, Hkv=16, d=128, causal=True, seed=10, B=2, N=16384),
     # long context on one GPU
     "fwd_causal_b1_h16_n131072_d128": Workload(
         "fwd_causal_b1_h16_n131072_d128", "fwd", Hq=16, Hkv=16, d=128, causal=True, seed=6, B=1, N=131072),
@@ -214,6 +249,68 @@ def make_split_inputs(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, causa
                        n_splits=n_splits)
 
 
+@dataclasses.dataclass
+class Fp8Inputs:
+    """Q, K as E4M3 codes (uint8) with per-(sequence, head) fp32 descales; V as bf16 bits."""
+    q8: np.ndarray
+    k8: np.ndarray
+    v: np.ndarray
+    q_descale: np.ndarray        # float32 [B, Hq]
+    k_descale: np.ndarray        # float32 [B, Hkv]
+    cu_seqlens: Optional[np.ndarray]
+    B: int
+    N: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    scale: float
+
+
+def _quantize_heads(x: np.ndarray, cu: Optional[np.ndarray], nseq: int):
+    """Per-(sequence, head) descale = amax / 448 and the E4M3 codes of x / descale."""
+    H = x.shape[-2]
+    ds = np.ones((nseq, H), dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    for s in range(nseq):
+        blk = x[s] if cu is None else x[int(cu[s]):int(cu[s + 1])]
+        if blk.size == 0:
+            continue
+        amax = np.max(np.abs(blk), axis=(0, 2))                       # [H]
+        ds[s] = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+        q = f32_to_e4m3_bits(blk / ds[s].astype(np.float64)[None, :, None])
+        if cu is None:
+            codes[s] = q
+        else:
+            codes[int(cu[s]):int(cu[s + 1])] = q
+    return codes, ds
+
+
+def make_fp8_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, causal: bool, seed: int,
+                    lengths: Optional[np.ndarray] = None, scale: Optional[float] = None) -> Fp8Inputs:
+    """Q, K, V drawn as for make_inputs; Q and K quantised to E4M3 per (sequence, head), V to bf16."""
+    rng = np.random.default_rng(seed)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    cu = None
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B, N = len(lengths), int(lengths.max()) if len(lengths) else 0
+        T = int(cu[-1])
+        qs, ks = (T, Hq, d), (T, Hkv, d)
+    else:
+        qs, ks = (B, N, Hq, d), (B, N, Hkv, d)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = _draw_bf16(rng, ks)
+    q8, qd = _quantize_heads(q, cu, B)
+    k8, kd = _quantize_heads(k, cu, B)
+    return Fp8Inputs(q8=q8, k8=k8, v=v, q_descale=qd, k_descale=kd, cu_seqlens=cu, B=B, N=N, Hq=Hq, Hkv=Hkv,
+                     d=d, causal=causal, scale=scale)
+
+
 def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
     """(query, key) pairs a split-KV problem computes: query i sees keys <= i + Nk - Nq when causal."""
     if not causal:
@@ -223,6 +320,8 @@ def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
 
 def workload_inputs(name: str) -> Inputs:
     w = WORKLOADS[name]
+    if w.kind == "fp8":
+        return make_fp8_inputs(w.B, w.N, w.Hq, w.Hkv, w.d, w.causal, w.seed, scale=w.scale)
     if w.kind == "split":
         return make_split_inputs(w.B, w.N, w.Nk, w.Hq, w.Hkv, w.d, w.causal, w.seed, w.n_splits, scale=w.scale)
     if w.varlen:

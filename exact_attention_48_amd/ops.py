@@ -114,3 +114,23 @@ def merge(o_part, lse_part, stream=None, out=None, lse=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_part.device)
     capi.fa_merge(o_part, lse_part, o, lse, n, B, H, N, d, stream)
     return o, lse
+
+
+def forward_fp8(q8, k8, v, q_descale, k_descale, causal: bool, scale: Optional[float] = None, cu_seqlens=None,
+                max_seqlen=None, stream=None):
+    """8-bit Q/K forward: q8/k8 uint8 E4M3 codes in the Q/K layouts, v bf16, fp32 descales
+    [B, Hq] and [B, Hkv]. Returns (O bf16, LSE fp32)."""
+    _check("q8", q8, torch.uint8)
+    _check("k8", k8, torch.uint8)
+    _check("v", v)
+    _check("q_descale", q_descale, torch.float32)
+    _check("k_descale", k_descale, torch.float32)
+    B, N, Hq, Hkv, d = _dims(q8, k8, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse_shape = (B, Hq, N) if cu_seqlens is None else (Hq, q8.shape[0])
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=q8.device)
+    capi.fa_fwd_fp8(q8, k8, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens,
+                    stream)
+    return o, lse

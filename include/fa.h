@@ -150,6 +150,24 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     void* stream);
 
 /*
+ * Forward attention with 8-bit Q and K (the low-precision variant of
+ * FlashAttention's lineage; podcast.app episode page, source list). Q and K
+ * hold OCP E4M3 codes (1 byte each, layouts as for fa_fwd); element values are
+ * code * q_descale[s, h] and code * k_descale[s, hkv] (fp32, one per sequence
+ * and head; s is the batch index, or the sequence index of a packed batch).
+ * V is bf16 and O, LSE are as for fa_fwd: the exact attention of the
+ * dequantised Q and K, computed with the scores from the 8-bit matrix cores
+ * (the products of E4M3 values are exact in the fp32 accumulation).
+ *   q_descale  fp32 [B, Hq], device
+ *   k_descale  fp32 [B, Hkv], device
+ *   d          128 only (other sizes return FA_ERR_UNSUPPORTED)
+ * Other arguments and errors as for fa_fwd.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                     const int32_t* cu_seqlens, void* stream);
+
+/*
  * Split-KV partial attention (uniform batches). The keys of every sequence are
  * cut into n_splits contiguous chunks of C = ceil(Nk / n_splits) keys (chunk p:
  * keys p*C .. min((p+1)*C, Nk) - 1; chunks past the end are empty). For every

@@ -290,3 +290,53 @@ def merge_partials(o_part: np.ndarray, lse_part: np.ndarray):
     coef = np.where(dead[None], 0.0, w / np.where(dead, 1.0, tot)[None])   # [n, B, H, N]
     o = np.einsum("pbhn,pbnhd->bnhd", coef, o_part)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 forward: Q and K in 8-bit floating point with per-(sequence, head)
+# scales, V in bf16.
+#
+# The pages name low-precision attention in FlashAttention's lineage
+# (podcast.app episode page, source list: "FlashAttention-3: Fast and Accurate
+# Attention with Asynchrony and Low Precision", and SageAttention2, which
+# quantises Q and K more coarsely than the P V product). They fix no format.
+# The reading here: Q and K are OCP E4M3 values (1 sign, 4 exponent bits with
+# bias 7, 3 mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN;
+# no infinities; largest finite 448), dequantised as x = e4m3 * descale with
+# one fp32 descale per (sequence, head); V stays bf16. What is computed is the
+# exact attention of those dequantised values.
+# ---------------------------------------------------------------------------
+
+def e4m3_to_float(bits: np.ndarray) -> np.ndarray:
+    """Decode OCP E4M3 bit patterns (uint8) to float64."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * val
+    return np.where((b & 0x7F) == 0x7F, np.nan, out)
+
+
+def attention_forward_fp8(q8: np.ndarray, k8: np.ndarray, v: np.ndarray, q_descale: np.ndarray,
+                          k_descale: np.ndarray, scale: float, causal: bool,
+                          cu_seqlens: Optional[np.ndarray] = None, rows: RowSelect = None):
+    """Exact attention of the dequantised FP8 inputs. Returns (O, LSE) in float64.
+
+    q8, k8: uint8 E4M3 in the Q / K layouts; v: float64 values in the V layout;
+    q_descale [B, Hq], k_descale [B, Hkv] (B = number of sequences when packed).
+    """
+    packed = cu_seqlens is not None
+    q = e4m3_to_float(q8)
+    k = e4m3_to_float(k8)
+    qd = np.asarray(q_descale, dtype=np.float64)
+    kd = np.asarray(k_descale, dtype=np.float64)
+    if packed:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        for s in range(len(cu) - 1):
+            q[cu[s]:cu[s + 1]] *= qd[s][None, :, None]
+            k[cu[s]:cu[s + 1]] *= kd[s][None, :, None]
+    else:
+        q *= qd[:, None, :, None]
+        k *= kd[:, None, :, None]
+    return attention_forward(q, k, v, scale, causal, cu_seqlens, rows)

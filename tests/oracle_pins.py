@@ -411,3 +411,82 @@ def pin_split(split, merge):
     l_a = _rand(rng, 1, 2, 3)
     o_m, l_m = merge(np.stack([o_a, np.zeros_like(o_a)]), np.stack([l_a, np.full_like(l_a, -np.inf)]))
     assert np.array_equal(l_m, l_a) and np.allclose(o_m, o_a, rtol=0, atol=1e-15), "merge with an empty part"
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) Q/K forward
+# ---------------------------------------------------------------------------
+
+# Values the OCP 8-bit floating point specification states for E4M3:
+# largest normal 448 (S.1111.110), smallest normal 2^-6 (S.0001.000),
+# largest subnormal 0.875 * 2^-6, smallest subnormal 2^-9, 1.0 (bias 7),
+# NaN for S.1111.111, and no infinities.
+E4M3_FIXED = {0x7E: 448.0, 0x08: 2.0 ** -6, 0x07: 0.875 * 2.0 ** -6, 0x01: 2.0 ** -9, 0x38: 1.0,
+              0x00: 0.0, 0xFE: -448.0, 0xBE: -1.75, 0xC0: -2.0, 0x3C: 1.5, 0x3F: 1.875, 0x40: 2.0}
+
+
+def _e4m3_py(code: int) -> float:
+    """Brute-force decode: the E4M3 value set enumerated binade by binade with math.ldexp."""
+    mag = code & 0x7F
+    table = [math.ldexp(m, -9) for m in range(8)]                        # subnormals and zero
+    for e in range(1, 16):
+        table += [math.ldexp(8 + m, e - 10) for m in range(8)]           # (1 + m/8) 2^(e-7)
+    v = table[mag]
+    return -v if code & 0x80 else v
+
+
+def pin_fp8(fwd8, decode):
+    """decode(bits) -> float64; fwd8(q8, k8, v, qd, kd, scale, causal, cu) -> (O, LSE).
+
+    The decoder matches the specification's stated values, is odd-symmetric,
+    strictly increasing over the finite positive codes with spacing 2^(e-10) in
+    binade e, and gives NaN exactly for S.1111.111. The forward equals brute
+    force (pure Python) on inputs dequantised code by code with their own
+    (sequence, head) scale, uniform and packed.
+    """
+    codes = np.arange(256, dtype=np.uint8)
+    vals = decode(codes)
+    for c, want in E4M3_FIXED.items():
+        assert vals[c] == want, ("E4M3 value", hex(c), vals[c], want)
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and np.sum(np.isnan(vals)) == 2, "E4M3 NaN codes"
+    pos = vals[1:0x7F]
+    assert np.all(np.diff(pos) > 0), "E4M3 positive codes must increase"
+    assert np.all(vals[0x80:0xFF] == -vals[0:0x7F]), "E4M3 sign symmetry"
+    for e in range(1, 15):
+        seg = vals[8 * e: 8 * e + 8]
+        assert np.all(np.diff(seg) == 2.0 ** (e - 10)), ("E4M3 spacing", e)
+    assert all(vals[c] == _e4m3_py(c) for c in range(256) if (c & 0x7F) != 0x7F), "E4M3 vs enumeration"
+
+    rng = np.random.default_rng(31)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for (B, N, Hq, Hkv, d, causal, lens) in [(2, 6, 4, 2, 5, True, None), (1, 7, 2, 1, 4, False, None),
+                                             (0, 0, 4, 2, 3, True, [3, 5, 1])]:
+        if lens is None:
+            qs, ks, nseq = (B, N, Hq, d), (B, N, Hkv, d), B
+            cu = None
+        else:
+            T = sum(lens)
+            qs, ks, nseq = (T, Hq, d), (T, Hkv, d), len(lens)
+            cu = _cu(lens)
+        q8 = rng.choice(finite, size=qs)
+        k8 = rng.choice(finite, size=ks)
+        v = _rand(rng, *ks)
+        qd = rng.uniform(0.002, 0.02, size=(nseq, Hq))
+        kd = rng.uniform(0.002, 0.02, size=(nseq, Hkv))
+        scale = 0.3
+        o, lse = fwd8(q8, k8, v, qd, kd, scale, causal, cu)
+        # dequantise code by code, each row with its own sequence's scales
+        qf = np.zeros(qs)
+        kf = np.zeros(ks)
+        for idx in np.ndindex(*qs):
+            s = idx[0] if cu is None else int(np.searchsorted(cu, idx[0], side="right") - 1)
+            qf[idx] = _e4m3_py(int(q8[idx])) * qd[s, idx[-2]]
+        for idx in np.ndindex(*ks):
+            s = idx[0] if cu is None else int(np.searchsorted(cu, idx[0], side="right") - 1)
+            kf[idx] = _e4m3_py(int(k8[idx])) * kd[s, idx[-2]]
+        if cu is None:
+            ob, lb = bruteforce.forward(qf.tolist(), kf.tolist(), v.tolist(), scale, causal)
+        else:
+            ob, lb = bruteforce.forward(qf.tolist(), kf.tolist(), v.tolist(), scale, causal, cu.tolist())
+        assert np.max(np.abs(o - np.array(ob))) < TOL, ("FP8 O vs brute force", B, N, causal, lens)
+        assert np.max(np.abs(lse - np.array(lb))) < TOL, ("FP8 LSE vs brute force", B, N, causal, lens)

@@ -20,7 +20,7 @@ A = 0x100000   # a 16-byte aligned fake device address (never dereferenced: vali
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -153,3 +153,21 @@ def merge(*, op=A, lp=A, o=A, lse=A, n=2, B=1, H=2, N=16, d=128):
 ])
 def test_merge_rejects(lib, kw, expect):
     assert merge(**kw) == expect
+
+
+def fp8(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, scale=0.1, cu=None):
+    return capi.fa_fwd_fp8(q, k, v, qd, kd, o, lse, B, Hq, Hkv, N, d, causal, scale, cu, stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=64), capi.FA_ERR_UNSUPPORTED),                    # 8-bit Q/K: d = 128 only
+    (dict(d=96), capi.FA_ERR_UNSUPPORTED),
+    (dict(qd=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(kd=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=3, Hkv=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(causal=3), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=0), capi.FA_OK),
+])
+def test_fp8_rejects(lib, kw, expect):
+    assert fp8(**kw) == expect

@@ -61,3 +61,14 @@ def test_scale_is_float32_rounded():
     assert I.WORKLOADS["fwd_b1_h2_n256_d64"].scale == 0.125
     s = I.WORKLOADS["fwd_b4_h16_n4096_d128"].scale
     assert s == float(np.float32(1 / np.sqrt(128)))
+
+
+def test_e4m3_encoder_round_trips_and_rounds_to_even():
+    import oracle
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_to_float(codes)
+    keep = ~np.isnan(vals) & (codes != 0x80)                # -0 encodes as +0
+    assert np.array_equal(I.f32_to_e4m3_bits(vals[keep]), codes[keep])
+    # halfway cases go to the even code; beyond 448 saturates
+    got = I.f32_to_e4m3_bits(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 500.0, -1e9, np.nan]))
+    assert got.tolist() == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0xFE, 0x7F]

@@ -117,3 +117,26 @@ def test_split_mutant_is_caught(name):
     exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
     with pytest.raises(AssertionError):
         pins.pin_split(mod.attention_forward_split, mod.merge_partials)
+
+
+FP8_MUTANTS = {
+    "exponent_bias_8": ("(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)",
+                        "(1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 8.0)"),
+    "subnormal_exponent": ("np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e == 0, m / 8.0 * 2.0 ** -7,"),
+    "mantissa_over_16": ("(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 16.0) * np.exp2"),
+    "nan_code_missed": ("return np.where((b & 0x7F) == 0x7F, np.nan, out)", "return out"),
+    "sign_dropped": ("sign = np.where(b & 0x80, -1.0, 1.0)", "sign = np.where(b & 0x80, 1.0, 1.0)"),
+    "q_descale_sequence_order": ("q *= qd[:, None, :, None]", "q *= qd[::-1][:, None, :, None]"),
+    "k_scaled_by_q_descale": ("k *= kd[:, None, :, None]", "k *= qd[:, None, :kd.shape[1], None]"),
+    "packed_descale_first_sequence": ("q[cu[s]:cu[s + 1]] *= qd[s][None, :, None]", "q[cu[s]:cu[s + 1]] *= qd[0][None, :, None]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name):
+    old, new = FP8_MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    with pytest.raises(AssertionError):
+        pins.pin_fp8(mod.attention_forward_fp8, mod.e4m3_to_float)

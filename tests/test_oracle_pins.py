@@ -67,3 +67,7 @@ def test_dq_rows_match_torch_autograd():
 
 def test_split_and_merge_pins():
     pins.pin_split(oracle.attention_forward_split, oracle.merge_partials)
+
+
+def test_fp8_pins():
+    pins.pin_fp8(oracle.attention_forward_fp8, oracle.e4m3_to_float)
