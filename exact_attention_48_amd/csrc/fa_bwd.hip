@@ -221,12 +221,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
       const int r0 = q0 + (wave & 1) * 32;
       const int r = min(r0 + lane, L - 1);
       const float* src = (wave < 2 ? p.lse2 : p.dsum) + lse_index(p, s, h, seq0, r0, T, VARLEN);
-      buf2lds4(buffer_rsrc(src), (unsigned)(r - r0) * 4u, stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128);
+      buf2lds4(buffer_rsrc_uniform(src), (unsigned)(r - r0) * 4u,
+               stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128);
     }
+    // (the compiler computes these addresses on the vector unit; the copies
+    // take them through readfirstlane)
     const char* qb = (const char*)p.q + ((long)seq0 * p.Hq + h) * D * 2;
     const char* ob = (const char*)p.dout + ((long)seq0 * p.Hq + h) * D * 2;
-    copy.issue(stage, qb, q_stride_b, q0, L);
-    copy.issue(stage + S::TILEB, ob, q_stride_b, q0, L);
+    copy.template issue<true>(stage, qb, q_stride_b, q0, L);
+    copy.template issue<true>(stage + S::TILEB, ob, q_stride_b, q0, L);
     if (++iss_qt == n_qt) {
       iss_qt = qt0;
       ++iss_g;
@@ -307,24 +310,44 @@ void bwd_dkdv_kernel(const BwdParams p) {
       lg[k] = *(const f32x4 FA_LDS*)(lz + (k >> 2) * 32 + (k & 3) * 8);
       dg[k] = *(const f32x4 FA_LDS*)(dz + (k >> 2) * 32 + (k & 3) * 8);
     };
-    float pv[2], dv2[2];
-    auto elem = [&](int e) __attribute__((always_inline)) {
+    // The 32 softmax elements run as a four-stage software pipeline, one step
+    // per element slot, so that no instruction of a slot waits on another one
+    // of the same slot: step t forms x_t = S c - LSE2 and dP_t - D (element t),
+    // p_{t-1} = exp2(x_{t-1}) (masked), dS_{t-2} = p_{t-2} (dP - D)_{t-2}, and
+    // packs the pair (t-4, t-3) to bf16 when t-3 is odd. Steps 32..34 follow
+    // the last MFMA slot.
+    float xa[4], dd[4], pp[4], ds4[4];
+    auto st1 = [&](int e) __attribute__((always_inline)) {
       const int qb = e >> 4, r = e & 15, k = e >> 2, u = e & 3;
       if (u == 0 && k + 1 < 8) g_fetch(k + 1);
-      float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][r], c, -lg[k][u]));
+      xa[e & 3] = __builtin_fmaf(sc[qb][r], c, -lg[k][u]);
+      dd[e & 3] = pc[qb][r] - dg[k][u];
+    };
+    auto st2 = [&](int e) __attribute__((always_inline)) {
+      float pe = __builtin_amdgcn_exp2f(xa[e & 3]);
       if constexpr (MASK) {
+        const int qb = e >> 4, r = e & 15;
         const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         const bool dead = (q >= L) || (CAUSAL && my_key > q);
         pe = dead ? 0.f : pe;
       }
-      pv[e & 1] = pe;
-      dv2[e & 1] = pe * (pc[qb][r] - dg[k][u]);
+      pp[e & 3] = pe;
+    };
+    auto st3 = [&](int e) __attribute__((always_inline)) { ds4[e & 3] = pp[e & 3] * dd[e & 3]; };
+    auto st4 = [&](int e) __attribute__((always_inline)) {
       if (e & 1) {
         // pair (e-1, e) -> positions of the B operand of key step t = qb*2 + (r/8)
+        const int qb = e >> 4, r = e & 15;
         const int t = qb * 2 + (r >> 3), pos = (r & 7) >> 1;
-        pb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(pv[0], pv[1]));
-        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
+        pb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(pp[(e - 1) & 3], pp[e & 3]));
+        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(ds4[(e - 1) & 3], ds4[e & 3]));
       }
+    };
+    auto step = [&](int t) __attribute__((always_inline)) {
+      if (t >= 3 && t < 35) st4(t - 3);
+      if (t >= 2 && t < 34) st3(t - 2);
+      if (t >= 1 && t < 33) st2(t - 1);
+      if (t < 32) st1(t);
     };
     bf16x8 qa[PF];
 #pragma unroll
@@ -339,9 +362,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
       else pre[j + PF - NA] = b_fetch(ct, j + PF - NA);
       a_step(sx, px, j, a);
 #pragma unroll
-      for (int x = 0; x < EPS; ++x) elem(j * EPS + x);
+      for (int x = 0; x < EPS; ++x) step(j * EPS + x);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int t = 32; t < 35; ++t) step(t);
   };
 
   // Phase B: dV^T += dO^T P, dK^T += Q^T dS for the current tile. Step i:

@@ -148,6 +148,16 @@ __device__ __forceinline__ bf16x8 lds_read16(const void FA_LDS* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
+// The same for a `base` that is equal in every lane but that the compiler may
+// have computed on the vector unit: the address goes through readfirstlane so
+// the descriptor is built in scalar registers (otherwise every load that uses
+// it is wrapped in a loop over the lanes' distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void* base) {
+  const unsigned long long a = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return buffer_rsrc((const void*)(((unsigned long long)hi << 32) | lo));
+}
 // `bytes` (4 or 16) per lane from rsrc + voffset into LDS: the 64 lanes fill
 // 64 * bytes of LDS starting at `lds` (wave-uniform), lane i at lds + bytes * i.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, void FA_LDS* lds) {

@@ -45,9 +45,12 @@ struct RowCopy {
   }
   // `base` points at token 0 of this head; rows r0 .. r0 + ROWS - 1. The
   // tile's first row is the (scalar) buffer base, so the per-lane offsets stay
-  // loop-invariant.
+  // loop-invariant. UNIFORM passes the base through readfirstlane, for callers
+  // whose address arithmetic the compiler places on the vector unit.
+  template <bool UNIFORM = false>
   __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int r0, int L) const {
-    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(base + (long)r0 * stride);
+    const char* b = base + (long)r0 * stride;
+    const __amdgpu_buffer_rsrc_t rsrc = UNIFORM ? buffer_rsrc_uniform(b) : buffer_rsrc(b);
     char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
     if (r0 + ROWS <= L) {
 #pragma unroll
