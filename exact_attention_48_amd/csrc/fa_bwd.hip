@@ -8,8 +8,9 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, all on the caller's stream:
-//   1. bwd_prep_kernel: D_i = rowsum(dO o O) and LSE_i * log2(e), fp32, into
-//      the workspace (HBM-bound, one pass); for packed batches also
+//   1. bwd_prep_kernel: -D_i = -rowsum(dO o O) and LSE_i * log2(e), fp32, into
+//      the workspace (HBM-bound, one pass; -D seeds the dP accumulators of
+//      kernel 2, so dP - D costs no instruction); for packed batches also
 //      bwd_sched_kernel, the order in which kernel 2 takes its work.
 //   2. bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128-key tile),
 //      one wave per SIMD. Each wave keeps 32 keys' K and V fragments and their
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, long t
       const long b = t / p.N, n = t - b * p.N;
       idx = (b * p.Hq + h) * p.N + n;
     }
-    p.dsum[idx] = acc;
+    p.dsum[idx] = -acc;
     p.lse2[idx] = p.lse[idx] * kLog2e;
   }
 }
@@ -255,20 +256,43 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // S, dP of one tile (phase-A MFMAs): slot j = (k-step j / 4, operand j % 4:
   // S block 0, S block 1, dP block 0, dP block 1).
   constexpr int NA = 4 * KSTEPS;
+  // Slot j < NA/2: S block j % 2, k-step j / 2 (Q operand); slot j >= NA/2:
+  // dP block j % 2, k-step (j - NA/2) / 2 (dO operand). The dP chains start
+  // from the tile's -D rows (`nd`), so their results are dP - D.
   auto a_fetch = [&](const char FA_LDS* tile, int j) __attribute__((always_inline)) {
-    const int ks = j >> 2, cc = j & 3;
-    return to.row_operand(tile + (cc >> 1) * S::TILEB, ks, cc & 1);
+    const int dp = j >= NA / 2, ks = (j - dp * (NA / 2)) >> 1;
+    return to.row_operand(tile + dp * S::TILEB, ks, j & 1);
   };
-  auto a_step = [&](f32x16 (&sx)[2], f32x16 (&px)[2], int j, const bf16x8& a) __attribute__((always_inline)) {
-    const int ks = j >> 2, cc = j & 3;
-    f32x16& acc = cc < 2 ? sx[cc & 1] : px[cc & 1];
-    const bf16x8& b = cc < 2 ? kf[ks] : vf[ks];
-    if (ks == 0) mfma_v_first(acc, a, b);
-    else mfma_v(acc, a, b);
+  auto a_step = [&](f32x16 (&sx)[2], f32x16 (&px)[2], int j, const bf16x8& a, const f32x16 (&nd)[2])
+                    __attribute__((always_inline)) {
+    const int dp = j >= NA / 2, ks = (j - dp * (NA / 2)) >> 1;
+    f32x16& acc = dp ? px[j & 1] : sx[j & 1];
+    const bf16x8& b = dp ? vf[ks] : kf[ks];
+    if (ks == 0) {
+      if (dp) mfma_v_init(acc, a, b, nd[j & 1]);
+      else mfma_v_first(acc, a, b);
+    } else {
+      mfma_v(acc, a, b);
+    }
+  };
+  // -D of a tile's rows in the accumulator layout: block qb, register r ->
+  // row 32 qb + 8 (r/4) + 4 hl + r%4
+  auto nd_fetch = [&](const char FA_LDS* tile, f32x16 (&nd)[2]) __attribute__((always_inline)) {
+    const float FA_LDS* dz = (const float FA_LDS*)(tile + S::LSEOFF + TROWS * 4 + lse_lane);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *(const f32x4 FA_LDS*)(dz + qb * 32 + g * 8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nd[qb][4 * g + u] = v[u];
+      }
   };
 
   // Phase A without softmax work (first tile).
   auto phase_a0 = [&](const char FA_LDS* tile, f32x16 (&sx)[2], f32x16 (&px)[2]) __attribute__((always_inline)) {
+    f32x16 nd[2];
+    nd_fetch(tile, nd);
     bf16x8 qa[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) qa[i] = a_fetch(tile, i);
@@ -276,7 +300,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
     for (int j = 0; j < NA; ++j) {
       const bf16x8 a = qa[j % PF];
       if (j + PF < NA) qa[j % PF] = a_fetch(tile, j + PF);
-      a_step(sx, px, j, a);
+      a_step(sx, px, j, a, nd);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -304,24 +328,22 @@ void bwd_dkdv_kernel(const BwdParams p) {
     else asm volatile("; unmasked tile");
     constexpr int EPS = 32 / NA;                 // softmax elements per MFMA slot
     const float FA_LDS* lz = (const float FA_LDS*)(ct + S::LSEOFF + lse_lane);
-    const float FA_LDS* dz = lz + TROWS;
-    f32x4 lg[8], dg[8];                          // LSE2 / D of the 8 row groups (qb, r/4)
+    f32x4 lg[8];                                 // LSE2 of the 8 row groups (qb, r/4)
     auto g_fetch = [&](int k) __attribute__((always_inline)) {
       lg[k] = *(const f32x4 FA_LDS*)(lz + (k >> 2) * 32 + (k & 3) * 8);
-      dg[k] = *(const f32x4 FA_LDS*)(dz + (k >> 2) * 32 + (k & 3) * 8);
     };
+    f32x16 nd[2];                                // -D of the next tile's rows (dP chain seeds)
     // The 32 softmax elements run as a four-stage software pipeline, one step
     // per element slot, so that no instruction of a slot waits on another one
-    // of the same slot: step t forms x_t = S c - LSE2 and dP_t - D (element t),
-    // p_{t-1} = exp2(x_{t-1}) (masked), dS_{t-2} = p_{t-2} (dP - D)_{t-2}, and
-    // packs the pair (t-4, t-3) to bf16 when t-3 is odd. Steps 32..34 follow
-    // the last MFMA slot.
-    float xa[4], dd[4], pp[4], ds4[4];
+    // of the same slot: step t forms x_t = S c - LSE2 (element t),
+    // p_{t-1} = exp2(x_{t-1}) (masked), dS_{t-2} = p_{t-2} (dP - D)_{t-2} (the
+    // dP accumulator already holds dP - D), and packs the pair (t-4, t-3) to
+    // bf16 when t-3 is odd. Steps 32..34 follow the last MFMA slot.
+    float xa[4], pp[4], ds4[4];
     auto st1 = [&](int e) __attribute__((always_inline)) {
       const int qb = e >> 4, r = e & 15, k = e >> 2, u = e & 3;
       if (u == 0 && k + 1 < 8) g_fetch(k + 1);
       xa[e & 3] = __builtin_fmaf(sc[qb][r], c, -lg[k][u]);
-      dd[e & 3] = pc[qb][r] - dg[k][u];
     };
     auto st2 = [&](int e) __attribute__((always_inline)) {
       float pe = __builtin_amdgcn_exp2f(xa[e & 3]);
@@ -333,7 +355,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
       }
       pp[e & 3] = pe;
     };
-    auto st3 = [&](int e) __attribute__((always_inline)) { ds4[e & 3] = pp[e & 3] * dd[e & 3]; };
+    auto st3 = [&](int e) __attribute__((always_inline)) { ds4[e & 3] = pp[e & 3] * pc[e >> 4][e & 15]; };
     auto st4 = [&](int e) __attribute__((always_inline)) {
       if (e & 1) {
         // pair (e-1, e) -> positions of the B operand of key step t = qb*2 + (r/8)
@@ -354,13 +376,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
     for (int i = 0; i < PF; ++i) qa[i] = a_fetch(nt, i);
     if (issue) issue_next(issue_stage);
     g_fetch(0);
+    nd_fetch(nt, nd);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const bf16x8 a = qa[j % PF];
       if (j + PF < NA) qa[j % PF] = a_fetch(nt, j + PF);
       else pre[j + PF - NA] = b_fetch(ct, j + PF - NA);
-      a_step(sx, px, j, a);
+      a_step(sx, px, j, a, nd);
 #pragma unroll
       for (int x = 0; x < EPS; ++x) step(j * EPS + x);
       __builtin_amdgcn_sched_barrier(0);
@@ -623,7 +646,7 @@ void bwd_dq_kernel(const BwdParams p, int n_qtiles) {
         const bool dead = (key >= L) || (CAUSAL && key > my_q[qb]);
         pe = dead ? 0.f : pe;
       }
-      dv2[e & 1] = pe * (pc[qb][r] - dq_d[qb]);
+      dv2[e & 1] = pe * (pc[qb][r] + dq_d[qb]);   // dq_d holds -D
       if (e & 1) dsb[qb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(dv2[0], dv2[1]));
     };
     bf16x8 qa[PF];

@@ -51,6 +51,10 @@ __device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const
 __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
+//   acc (VGPR) = A * B + C, B held in AGPRs, C a VGPR tuple (left unchanged)
+__device__ __forceinline__ void mfma_v_init(f32x16& acc, const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(a), "a"(b), "v"(c));
+}
 //   acc (AGPR) += A * B, A and B in VGPRs
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));

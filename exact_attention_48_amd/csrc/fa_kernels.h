@@ -49,7 +49,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   const int32_t* cu_seqlens;
-  float* dsum;                 // workspace: D_i = rowsum(dO * O), laid out like LSE
+  float* dsum;                 // workspace: -D_i = -rowsum(dO * O), laid out like LSE
   float* lse2;                 // workspace: LSE_i * log2(e), laid out like LSE
   int* kt_prefix;              // workspace (packed batches): dK/dV schedule, see bwd_sched_kernel
   int kv_chunks;               // tile residues per (sequence, K/V head): 8 / gcd(Hkv, 8)
