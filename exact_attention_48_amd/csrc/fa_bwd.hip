@@ -251,6 +251,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   }
   f32x16 sA[2], pA[2], sB[2], pB[2];             // S, dP of two consecutive tiles (by tile parity)
   u32x4 pb[4], dsb[4];                           // P, dS (bf16 pairs) of the current tile
+  float pf[32];                                  // P of the current tile, fp32 (phase A -> phase B)
   const float c = p.scale_log2;
 
   // S, dP of one tile (phase-A MFMAs): slot j = (k-step j / 4, operand j % 4:
@@ -313,9 +314,11 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // reads; the last PF slots also read the first PF transposed operands of
   // phase B (`pre`).
   constexpr int NB = 8 * DBLK;
+  // phase B step i < NB/2: dV (dO^T operand), i >= NB/2: dK (Q^T operand);
+  // key step t = (i mod NB/2) / DBLK, d-block db = i mod DBLK
   auto b_fetch = [&](const char FA_LDS* ct, int i) __attribute__((always_inline)) {
-    const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
-    return to.tr_operand(ct + ((i & 1) ? 0 : S::TILEB), t, db);
+    const int dv_step = i < NB / 2, ii = i % (NB / 2);
+    return to.tr_operand(ct + (dv_step ? S::TILEB : 0), ii / DBLK, ii % DBLK);
   };
   auto phase_a = [&](auto mask_tag, const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2],
                      f32x16 (&px)[2], const f32x16 (&sc)[2], const f32x16 (&pc)[2], int q0, bool issue,
@@ -333,13 +336,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
       lg[k] = *(const f32x4 FA_LDS*)(lz + (k >> 2) * 32 + (k & 3) * 8);
     };
     f32x16 nd[2];                                // -D of the next tile's rows (dP chain seeds)
-    // The 32 softmax elements run as a four-stage software pipeline, one step
-    // per element slot, so that no instruction of a slot waits on another one
-    // of the same slot: step t forms x_t = S c - LSE2 (element t),
-    // p_{t-1} = exp2(x_{t-1}) (masked), dS_{t-2} = p_{t-2} (dP - D)_{t-2} (the
-    // dP accumulator already holds dP - D), and packs the pair (t-4, t-3) to
-    // bf16 when t-3 is odd. Steps 32..34 follow the last MFMA slot.
-    float xa[4], pp[4], ds4[4];
+    // The 32 elements of P run as a three-stage software pipeline, one step per
+    // element slot, so that no instruction of a slot waits on another one of
+    // the same slot: step t forms x_t = S c - LSE2 (element t), p_{t-1} =
+    // exp2(x_{t-1}) (masked, kept in fp32 for phase B), and packs the pair
+    // (t-3, t-2) to bf16 when t-2 is odd. Steps 32 and 33 follow the last MFMA
+    // slot. dS = P (dP - D) is left to phase B, whose MFMAs have no other VALU
+    // work beside them.
+    float xa[4];
     auto st1 = [&](int e) __attribute__((always_inline)) {
       const int qb = e >> 4, r = e & 15, k = e >> 2, u = e & 3;
       if (u == 0 && k + 1 < 8) g_fetch(k + 1);
@@ -353,20 +357,16 @@ void bwd_dkdv_kernel(const BwdParams p) {
         const bool dead = (q >= L) || (CAUSAL && my_key > q);
         pe = dead ? 0.f : pe;
       }
-      pp[e & 3] = pe;
+      pf[e] = pe;
     };
-    auto st3 = [&](int e) __attribute__((always_inline)) { ds4[e & 3] = pp[e & 3] * pc[e >> 4][e & 15]; };
-    auto st4 = [&](int e) __attribute__((always_inline)) {
+    auto st3 = [&](int e) __attribute__((always_inline)) {
       if (e & 1) {
         // pair (e-1, e) -> positions of the B operand of key step t = qb*2 + (r/8)
         const int qb = e >> 4, r = e & 15;
-        const int t = qb * 2 + (r >> 3), pos = (r & 7) >> 1;
-        pb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(pp[(e - 1) & 3], pp[e & 3]));
-        dsb[t][pos] = __builtin_bit_cast(unsigned, pack_bf16(ds4[(e - 1) & 3], ds4[e & 3]));
+        pb[qb * 2 + (r >> 3)][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(pf[e - 1], pf[e]));
       }
     };
     auto step = [&](int t) __attribute__((always_inline)) {
-      if (t >= 3 && t < 35) st4(t - 3);
       if (t >= 2 && t < 34) st3(t - 2);
       if (t >= 1 && t < 33) st2(t - 1);
       if (t < 32) st1(t);
@@ -389,21 +389,53 @@ void bwd_dkdv_kernel(const BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int t = 32; t < 35; ++t) step(t);
+    for (int t = 32; t < 34; ++t) step(t);
   };
 
-  // Phase B: dV^T += dO^T P, dK^T += Q^T dS for the current tile. Step i:
-  // key step t = i / (2 DBLK), d-block db = (i / 2) % DBLK, dV (even i) or dK.
-  // `qa` holds the operands of steps 0 .. PF-1 (read during phase A).
-  auto phase_b = [&](const char FA_LDS* ct, bf16x8 (&qa)[PF]) __attribute__((always_inline)) {
+  // Phase B: dV^T += dO^T P (steps 0 .. NB/2-1), then dK^T += Q^T dS (steps
+  // NB/2 .. NB-1) for the current tile; `qa` holds the transposed operands of
+  // steps 0 .. PF-1 (read during phase A). Beside the dV MFMAs the VALU forms
+  // dS = P (dP - D) (pc holds dP - D) and packs it, a two-stage pipeline over
+  // the 16 element pairs: the products of pairs 2j, 2j+1 at one step, their
+  // bf16 packs at the next.
+  auto phase_b = [&](const char FA_LDS* ct, bf16x8 (&qa)[PF], const f32x16 (&pc)[2]) __attribute__((always_inline)) {
+    constexpr int NH = NB / 2;
+    constexpr int PPS = 16 / NH;                 // element pairs per dV step
+    float dsv[2][2 * PPS];
+    auto ds_mul = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < PPS; ++x) {
+        const int e = 2 * (st * PPS + x);
+        dsv[st & 1][2 * x] = pf[e] * pc[e >> 4][e & 15];
+        dsv[st & 1][2 * x + 1] = pf[e + 1] * pc[(e + 1) >> 4][(e + 1) & 15];
+      }
+    };
+    auto ds_pack = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < PPS; ++x) {
+        const int e = 2 * (st * PPS + x), qb = e >> 4, r = e & 15;
+        dsb[qb * 2 + (r >> 3)][(r & 7) >> 1] =
+            __builtin_bit_cast(unsigned, pack_bf16(dsv[st & 1][2 * x], dsv[st & 1][2 * x + 1]));
+      }
+    };
     asm volatile("s_nop 2");   // VALU-written B operands -> first MFMA
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const bf16x8 a = qa[i % PF];
       if (i + PF < NB) qa[i % PF] = b_fetch(ct, i + PF);
-      const int t = i / (2 * DBLK), db = (i >> 1) % DBLK;
-      if (i & 1) mfma_a(dk[db], a, __builtin_bit_cast(bf16x8, dsb[t]));
-      else mfma_a(dv[db], a, __builtin_bit_cast(bf16x8, pb[t]));
+      if (i < NH) {
+        const int t = i / DBLK, db = i % DBLK;
+        mfma_a(dv[db], a, __builtin_bit_cast(bf16x8, pb[t]));
+        if (i >= 1) ds_pack(i - 1);
+        ds_mul(i);
+      } else {
+        if (i == NH) {
+          ds_pack(NH - 1);
+          asm volatile("s_nop 2");               // VALU-written dS -> dK MFMA
+        }
+        const int t = (i - NH) / DBLK, db = (i - NH) % DBLK;
+        mfma_a(dk[db], a, __builtin_bit_cast(bf16x8, dsb[t]));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -436,11 +468,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
     if constexpr (BI % 2 == 0) {
       if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0, issue, nst, pre);
       else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sB, pB, sA, pA, q0, issue, nst, pre);
+      phase_b(stg[BI], pre, pA);
     } else {
       if (need_mask) phase_a(ic<1>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0, issue, nst, pre);
       else phase_a(ic<0>{}, stg[(BI + 1) % NSTAGE], stg[BI], sA, pA, sB, pB, q0, issue, nst, pre);
+      phase_b(stg[BI], pre, pB);
     }
-    phase_b(stg[BI], pre);
   };
   for (int i = 0; i < n_it; i += NSTAGE) {
     iter(ic<0>{}, i);
