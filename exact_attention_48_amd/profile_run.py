@@ -6,6 +6,10 @@ Meant to run under ``rocprofv3 --pmc ...`` (or ``--kernel-trace``):
 
 --part fwd    fa_fwd on the workload's shape
 --part bwd    fa_fwd once, then fa_bwd `reps` times
+--part split  fa_fwd_split (the workload's chunk count) then fa_merge, `reps` times
+              (split-KV workloads)
+--part fp8    fa_fwd_fp8 `reps` times (8-bit Q/K workloads; E4M3 codes from a
+              scaled N(0,1) draw, descale 1/64)
 --part copy   a plain device-to-device copy of 512 MiB (known byte count, used
               to calibrate FETCH_SIZE / WRITE_SIZE against real HBM bytes)
 Inputs are seeded N(0,1) bf16 drawn on the GPU with the workload's shapes.
@@ -24,7 +28,7 @@ from . import capi, inputs as I
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="fwd_b4_h16_n4096_d128", choices=sorted(I.WORKLOADS))
-    ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "copy"])
+    ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "split", "fp8", "copy"])
     ap.add_argument("--reps", type=int, default=3)
     args = ap.parse_args()
     dev = torch.device("cuda:0")
@@ -39,6 +43,37 @@ def main():
     w = I.WORKLOADS[args.workload]
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
+    rnd = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    if args.part == "split":
+        if w.kind != "split":
+            raise SystemExit("--part split needs a split-KV workload")
+        q = rnd((w.B, w.N, w.Hq, w.d))
+        k, v = rnd((w.B, w.Nk, w.Hkv, w.d)), rnd((w.B, w.Nk, w.Hkv, w.d))
+        op = torch.empty((w.n_splits, w.B, w.N, w.Hq, w.d), dtype=torch.float32, device=dev)
+        lp = torch.empty((w.n_splits, w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        o = torch.empty((w.B, w.N, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.reps):
+            capi.fa_fwd_split(q, k, v, op, lp, w.B, w.Hq, w.Hkv, w.N, w.Nk, w.d, int(w.causal), w.scale, w.n_splits)
+            capi.fa_merge(op, lp, o, lse, w.n_splits, w.B, w.Hq, w.N, w.d)
+        torch.cuda.synchronize()
+        print(f"split x {args.reps} on {args.workload} done")
+        return
+    if args.part == "fp8":
+        if w.kind != "fp8":
+            raise SystemExit("--part fp8 needs an 8-bit workload")
+        q8 = (rnd((w.B, w.N, w.Hq, w.d)).float() * 64).to(torch.float8_e4m3fn).view(torch.uint8)
+        k8 = (rnd((w.B, w.N, w.Hkv, w.d)).float() * 64).to(torch.float8_e4m3fn).view(torch.uint8)
+        v = rnd((w.B, w.N, w.Hkv, w.d))
+        qd = torch.full((w.B, w.Hq), 1.0 / 64, dtype=torch.float32, device=dev)
+        kd = torch.full((w.B, w.Hkv), 1.0 / 64, dtype=torch.float32, device=dev)
+        o = torch.empty((w.B, w.N, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        for _ in range(args.reps):
+            capi.fa_fwd_fp8(q8, k8, v, qd, kd, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale)
+        torch.cuda.synchronize()
+        print(f"fp8 x {args.reps} on {args.workload} done")
+        return
     if w.varlen:
         lens = I.draw_lengths(np.random.default_rng(w.seed), w.B, w.len_lo, w.len_hi)
         cu_h = np.zeros(len(lens) + 1, dtype=np.int32)
@@ -50,7 +85,6 @@ def main():
         N = w.N
         qs, ks, lse_shape = (w.B, N, w.Hq, w.d), (w.B, N, w.Hkv, w.d), (w.B, w.Hq, N)
         cu = None
-    rnd = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     q, k, v = rnd(qs), rnd(ks), rnd(ks)
     o = torch.empty_like(q)
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
