@@ -169,7 +169,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // fa_order.h describes ----
   TileItem item;
   if constexpr (VARLEN) {
-    if (!kv_item_xcd(blockIdx.x, p.B, p.Hkv, p.kv_chunks, p.kt_prefix, item)) return;
+    if (!kv_item_xcd(blockIdx.x, p.B, p.Hkv, p.kv_chunks, (p.N + KV_BN - 1) / KV_BN, p.kt_prefix, item)) return;
   } else {
     if (!kv_item_level(blockIdx.x, p.B, p.Hkv, (p.N + KV_BN - 1) / KV_BN, item)) return;
   }

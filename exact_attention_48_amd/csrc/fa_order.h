@@ -97,8 +97,9 @@ inline long kv_grid_xcd(int B, int Hkv, int nc, int n_kt) {
 // Packed batches: `prefix` (nc rows of B + 1) gives, for residue i and
 // sequence s, the key tiles kt = i (mod nc) of sequences 0 .. s-1, so the
 // workgroup finds its sequence by binary search and no workgroup is spent on
-// tiles past a sequence's end.
-__device__ __forceinline__ bool kv_item_xcd(int b, int B, int Hkv, int nc, const int* prefix, TileItem& it) {
+// tiles past a sequence's end. n_kt bounds every sequence's key tiles.
+__device__ __forceinline__ bool kv_item_xcd(int b, int B, int Hkv, int nc, int n_kt, const int* prefix,
+                                            TileItem& it) {
   const int xcd = b & 7, j = b >> 3;
   const int ci = xcd % nc;
   const int m = Hkv * nc / 8;                      // K/V heads per sequence on this XCD
@@ -114,8 +115,8 @@ __device__ __forceinline__ bool kv_item_xcd(int b, int B, int Hkv, int nc, const
   const int jj = j - m * P[lo];
   // a table the preparation kernel did not write cannot send a workgroup
   // outside the problem: out-of-range entries end it here (or at the caller's
-  // tile-past-the-end check)
-  if (cnt <= 0 || jj < 0 || jj >= m * cnt) return false;
+  // tile-past-the-end check, which the bound on cnt keeps free of overflow)
+  if (cnt <= 0 || cnt > (n_kt + nc - 1) / nc || jj < 0 || jj >= m * cnt) return false;
   const int u = jj / cnt;
   it.s = lo;
   it.h = xcd / nc + (8 / nc) * u;
