@@ -10,7 +10,7 @@
 namespace {
 
 constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kDefaultTau = 8.0f;
+constexpr float kDefaultTau = 32.0f;
 
 inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 

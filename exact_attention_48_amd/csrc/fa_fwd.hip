@@ -12,13 +12,14 @@
 //     -> every lane holds the scores of ONE query for 16 of the tile's keys,
 //        so a row max is an in-lane max plus one v_permlane32_swap
 //   masking only on tiles that cross the causal diagonal or the sequence end
-//   conditional rescaling: each row's max m stays at its first tile's max;
-//     a tile whose max exceeds m by more than tau (log2 units) only raises a
-//     flag, and a workgroup with a raised flag runs its loop a second time
-//     with the exact row maxima (the threshold-gated rescale of the pages,
-//     daily.dev "Summary" and the FA4 abstract on the zhuanzhiai.com page,
-//     moved out of the loop: O and l always share the same m, so no pass
-//     ever rescales O)
+//   conditional rescaling: each row's max m stays at its first tile's max,
+//     so O and l always share one m and no pass ever rescales O; the loop
+//     takes no further maxima. A row sum l above 2^tau (log2 units) at the
+//     end -- the only way a later score can have outgrown m far enough to
+//     threaten fp32 -- sends the workgroup through a pass that records the
+//     true row maxima and a last pass with them (the threshold-gated rescale
+//     of the pages, daily.dev "Summary" and the FA4 abstract on the
+//     zhuanzhiai.com page, with the test moved out of the loop)
 //   P = exp2(S c - m c), c = scale * log2(e), hardware v_exp_f32 or the
 //     FMA-pipe polynomial (software exponential: daily.dev "Summary")
 //   l += rowsum(P) (per-lane partial sums, combined once at the end)
@@ -31,11 +32,11 @@
 //
 // Software pipeline (the MMA/softmax overlap of the pages' pipeline, daily.dev
 // "Summary"), iteration j of a wave, one MFMA stream:
-//   phase A : S of tile j+1 (16 MFMAs), interleaved with the exps of tile j
-//             for query block 0 and half of block 1;
+//   phase A : S of tile j+1 (16 MFMAs), interleaved with exps of tile j
+//             (the rest of query block 0 and part of block 1);
 //   phase B1: O_0 += V_j P_0 (8 MFMAs), with the other exps of block 1;
-//   phase B2: O_1 += V_j P_1 (8 MFMAs), with the masking, row maxima and
-//             threshold checks of tile j+1 (its S is done by then).
+//   phase B2: O_1 += V_j P_1 (8 MFMAs), with the masking of tile j+1 (its S
+//             is done by then) and its first exps.
 //
 // K and V tiles travel HBM -> LDS with buffer_load ... lds (no register
 // staging) through a 4-deep ring of distinct LDS objects, issued two
@@ -183,10 +184,27 @@ void fa_fwd_kernel(const FwdParams p) {
   RCV vcopy;
   kcopy.init(wave, lane, (unsigned)k_stride);
   vcopy.init(wave, lane, (unsigned)kv_stride);
+  // tile copies in order: the next tile starts at key kb + iss * BN, whose
+  // K and V rows are at kcur and vcur
   int iss = 0;
+  const char* kcur = kbase;
+  const char* vcur = vbase;
+  auto restart_copies = [&]() __attribute__((always_inline)) {
+    iss = 0;
+    kcur = kbase + (long)kb * k_stride;
+    vcur = vbase + (long)kb * kv_stride;
+  };
   auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
-    kcopy.issue(stage, kbase, k_stride, kb + iss * BN, ke);
-    vcopy.issue(stage + S::VOFF, vbase, kv_stride, kb + iss * BN, ke);
+    const int r0 = kb + iss * BN;
+    if (r0 + BN <= ke) {
+      kcopy.issue_full(stage, kcur);
+      vcopy.issue_full(stage + S::VOFF, vcur);
+    } else {
+      kcopy.issue_tail(stage, kcur, k_stride, ke - 1 - r0);
+      vcopy.issue_tail(stage + S::VOFF, vcur, kv_stride, ke - 1 - r0);
+    }
+    kcur += BN * k_stride;
+    vcur += BN * kv_stride;
     ++iss;
   };
 
@@ -284,16 +302,21 @@ void fa_fwd_kernel(const FwdParams p) {
     over[qb] = over[qb] || ((mx - m_run[qb]) * c > tau);   // false when both are -inf
   };
   // ---- one iteration's MFMA stream ----
-  // Softmax work of the current tile (S^T in sc), spread over the MFMA slots:
-  //   phase A : exp pipeline steps 0..UA-1 (query block 0 and half of block 1)
-  //   phase B1: exp pipeline steps UA..33 (the rest of block 1; P of block 0
-  //             is complete after step 17, so phase B1 can start)
-  //   phase B2: masking / maxima / decisions of the next tile (S^T in sx)
-  constexpr int UA = 24;
-  constexpr int UB = 34 - UA;
+  // The 34 exp pipeline steps of a tile are spread over three phases:
+  //   phase B2 of the previous iteration: steps 0..KB2-1, right after the
+  //             tile's masking (its S^T is complete by then);
+  //   phase A : steps KB2..KB2+UA-1 beside the S^T MFMAs of the next tile
+  //             (P of query block 0 is complete after step 17);
+  //   phase B1: the rest, beside O_0 += V^T P_0 (P of block 1 complete
+  //             after step 33, before phase B2 needs it).
+  // Row maxima of every tile are taken only in a tracking pass (see below).
+  constexpr int KB2 = 12;
+  constexpr int UA = 16;
+  constexpr int UB = 34 - KB2 - UA;
+  static_assert(KB2 + UA >= 18 && UB >= 0, "P of query block 0 must be complete before phase B1");
   constexpr int VPRE = (PFA < NV) ? PFA : NV;       // V^T fragments read during phase A
   auto stream = [&](const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2], const f32x16 (&sc)[2],
-                    int k_next, bool issue, char FA_LDS* issue_stage) __attribute__((always_inline)) {
+                    int k_next, bool issue, char FA_LDS* issue_stage, bool track) __attribute__((always_inline)) {
     AFrag qa[PFA];
 #pragma unroll
     for (int i = 0; i < PFA; ++i) qa[i] = a_frag(nt, i);
@@ -311,7 +334,7 @@ void fa_fwd_kernel(const FwdParams p) {
         const int j = 2 * ks + x;
         a_step(sx, j, a);
 #pragma unroll
-        for (int t = UA * j / NA; t < UA * (j + 1) / NA; ++t) exp_step(sc, t);
+        for (int t = KB2 + UA * j / NA; t < KB2 + UA * (j + 1) / NA; ++t) exp_step(sc, t);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -322,28 +345,29 @@ void fa_fwd_kernel(const FwdParams p) {
       if (f + VPRE < NV) vf[f + VPRE] = v_frag(ct, f + VPRE);
       mfma_a(oacc[0][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[0][f / DBLK]));
 #pragma unroll
-      for (int t = UA + UB * f / NV; t < UA + UB * (f + 1) / NV; ++t) exp_step(sc, t);
+      for (int t = KB2 + UA + UB * f / NV; t < KB2 + UA + UB * (f + 1) / NV; ++t) exp_step(sc, t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // phase B2: O_1 += V^T P_1, with the next tile's masking, maxima, decisions
+    // phase B2: O_1 += V^T P_1, with the next tile's masking (and, in a
+    // tracking pass, its maxima) and its first exp steps. On the last
+    // iteration the next tile lies past every visible key, so the masking
+    // turns all of its scores into -inf and its steps add nothing.
     asm volatile("s_nop 2");
     const bool mask_next = needs_mask(k_next);
 #pragma unroll
     for (int f = 0; f < NV; ++f) {
       mfma_a(oacc[1][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[1][f / DBLK]));
-      // work item w of the 6: mask+max(0, lo), max(0, hi), decide(0), max(1, lo), max(1, hi), decide(1)
-#pragma unroll
-      for (int wi = 6 * f / NV; wi < 6 * (f + 1) / NV; ++wi) {
-        if (wi == 0) {
-          if (mask_next) mask_tile(sx, k_next);
-          max_half(sx, 0, 0);
-        }
-        if (wi == 1) max_half(sx, 0, 1);
-        if (wi == 2) decide(0);
-        if (wi == 3) max_half(sx, 1, 0);
-        if (wi == 4) max_half(sx, 1, 1);
-        if (wi == 5) decide(1);
+      if (f == 0 && mask_next) mask_tile(sx, k_next);
+      if (f == 1 && track) {
+        max_half(sx, 0, 0);
+        max_half(sx, 0, 1);
+        max_half(sx, 1, 0);
+        max_half(sx, 1, 1);
+        decide(0);
+        decide(1);
       }
+#pragma unroll
+      for (int t = KB2 * f / NV; t < KB2 * (f + 1) / NV; ++t) exp_step(sx, t);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -352,7 +376,7 @@ void fa_fwd_kernel(const FwdParams p) {
   // parity i), tile i+1 in stage BI+1; tile i+3 is copied into stage BI+3 (last
   // read as tile i-1, before this iteration's barrier). The S^T MFMAs of tile
   // i+1 also run on the last iteration (stale LDS, results unused).
-  auto iter = [&](auto bi_tag, const int i) __attribute__((always_inline)) {
+  auto iter = [&](auto bi_tag, const int i, const bool track) __attribute__((always_inline)) {
     constexpr int BI = decltype(bi_tag)::value;
     if (i + 2 < n_it) wait_vm(OPS);
     else if (i + 1 < n_it) wait_vm(0);
@@ -360,16 +384,17 @@ void fa_fwd_kernel(const FwdParams p) {
     const bool issue = i + 3 < n_it;
     char FA_LDS* const nst = stage((BI + 3) % NSTAGE);
     const int k_next = kb + (i + 1) * BN;
-    if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, k_next, issue, nst);
-    else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, k_next, issue, nst);
+    if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, k_next, issue, nst, track);
+    else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, k_next, issue, nst, track);
   };
 
-  // Rescaling, taken out of the loop: in the first pass each row's max is
-  // fixed at its first tile's max, and every later tile only records its true
-  // max and whether it exceeded the fixed one by more than tau (log2 units).
-  // If none did (the common case) O and l share that max, every P is at most
-  // 2^tau, and the pass is exact. Otherwise the workgroup runs the loop again
-  // with each row's true maximum, where no rescaling can be needed.
+  // Rescaling, taken out of the loop. In the first pass each row's max m is
+  // fixed at its first tile's max, and O and l share it, so the pass is exact
+  // whatever the later scores are, as long as nothing overflows. Every P is
+  // at most the row sum l, so a row sum of at most 2^tau (tau in log2 units)
+  // bounds every P, and with it O, far inside fp32. A row above that (or not
+  // finite) sends the workgroup through a tracking pass that records each
+  // row's true max, and then a last pass with that max, where every P <= 1.
   __shared__ int over_flag[NWAVES];
   bool run = true;
   if constexpr (SPLIT) {
@@ -384,8 +409,10 @@ void fa_fwd_kernel(const FwdParams p) {
       }
     }
   }
+  const float l_limit = exp2f(tau);
   for (int pass = 0; run; ++pass) {
-    iss = 0;
+    const bool track = pass == 1;
+    restart_copies();
     issue_next(stage(0));
     if (n_it > 1) issue_next(stage(1));
     if (n_it > 2) issue_next(stage(2));
@@ -394,12 +421,12 @@ void fa_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
       l_run[qb] = 0.f;
-      m_run[qb] = pass == 0 ? -INFINITY : m_seen[qb];
+      m_run[qb] = pass == 2 ? m_seen[qb] : -INFINITY;
       m_seen[qb] = -INFINITY;
       over[qb] = false;
     }
 
-    // ---- prologue: tile 0 in, S^T of tile 0 and its maxima ----
+    // ---- prologue: tile 0 in, S^T of tile 0, its maxima and first exp steps ----
     if (n_it > 2) wait_vm(2 * OPS);
     else if (n_it > 1) wait_vm(OPS);
     else wait_vm(0);
@@ -427,15 +454,17 @@ void fa_fwd_kernel(const FwdParams p) {
     for (int qb = 0; qb < 2; ++qb) {
       const float mx = pair_max(mpart[qb]);
       m_seen[qb] = mx;
-      if (pass == 0) m_run[qb] = mx;
+      if (pass < 2) m_run[qb] = mx;
       mc[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb] * c;
     }
+#pragma unroll
+    for (int t = 0; t < KB2; ++t) exp_step(sA, t);
 
     for (int i = 0; i < n_it; i += NSTAGE) {
-      iter(ic<0>{}, i);
-      if (i + 1 < n_it) iter(ic<1>{}, i + 1);
-      if (i + 2 < n_it) iter(ic<2>{}, i + 2);
-      if (i + 3 < n_it) iter(ic<3>{}, i + 3);
+      iter(ic<0>{}, i, track);
+      if (i + 1 < n_it) iter(ic<1>{}, i + 1, track);
+      if (i + 2 < n_it) iter(ic<2>{}, i + 2, track);
+      if (i + 3 < n_it) iter(ic<3>{}, i + 3, track);
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -443,7 +472,13 @@ void fa_fwd_kernel(const FwdParams p) {
       keep_live(sB[x]);
     }
     mfma_result_wait();
-    if (pass == 1) break;
+    if (pass == 2) break;
+    if (pass == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) over[qb] = !(pair_sum(l_run[qb]) <= l_limit);
+    } else {
+      over[0] = true;                 // after the tracking pass, the exact pass
+    }
     // all copies have landed (the last iterations wait for them); LDS is free
     // once every wave is past this point
     const bool any = wave_any(over[0] || over[1]);

@@ -50,18 +50,26 @@ struct RowCopy {
   template <bool UNIFORM = false>
   __device__ __forceinline__ void issue(char FA_LDS* tile, const char* base, long stride, int r0, int L) const {
     const char* b = base + (long)r0 * stride;
+    if (r0 + ROWS <= L) issue_full<UNIFORM>(tile, b);
+    else issue_tail<UNIFORM>(tile, b, stride, L - 1 - r0);
+  }
+  // A whole tile whose first row is at `b`.
+  template <bool UNIFORM = false>
+  __device__ __forceinline__ void issue_full(char FA_LDS* tile, const char* b) const {
     const __amdgpu_buffer_rsrc_t rsrc = UNIFORM ? buffer_rsrc_uniform(b) : buffer_rsrc(b);
     char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
-    if (r0 + ROWS <= L) {
 #pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) buf2lds16(rsrc, off[u], dst + u * 1024);
-    } else {
-      const int last = L - 1 - r0;
+    for (int u = 0; u < PER_WAVE; ++u) buf2lds16(rsrc, off[u], dst + u * 1024);
+  }
+  // The last tile of a sequence: rows past `last` (relative to `b`) repeat it.
+  template <bool UNIFORM = false>
+  __device__ __forceinline__ void issue_tail(char FA_LDS* tile, const char* b, long stride, int last) const {
+    const __amdgpu_buffer_rsrc_t rsrc = UNIFORM ? buffer_rsrc_uniform(b) : buffer_rsrc(b);
+    char FA_LDS* dst = tile + wave * PER_WAVE * 1024;
 #pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        const int r = min(row(u), last);
-        buf2lds16(rsrc, (unsigned)r * (unsigned)stride + chunk16(u), dst + u * 1024);
-      }
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int r = min(row(u), last);
+      buf2lds16(rsrc, (unsigned)r * (unsigned)stride + chunk16(u), dst + u * 1024);
     }
   }
 };

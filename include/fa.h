@@ -69,11 +69,13 @@ typedef enum {
 /* Optional tuning knobs of the forward pass; pass NULL for the defaults. */
 typedef struct {
     int exp_mode;        /* fa_exp_mode; default FA_EXP_HW */
-    float rescale_tau;   /* conditional rescaling threshold in log2 units: the running
-                            max, and with it O and the row sum, is only updated when it
-                            grows by more than tau ("conditional online softmax
-                            rescaling", daily.dev "Summary"). Default 8. Any tau >= 0
-                            gives the same result up to rounding. */
+    float rescale_tau;   /* conditional rescaling threshold in log2 units ("conditional
+                            online softmax rescaling", daily.dev "Summary"): each row
+                            keeps its first key tile's max, and only a row whose sum of
+                            exp2 terms relative to that max exceeds 2^tau (or is not
+                            finite) is recomputed with its exact max. Default 32, which
+                            bounds every P by 2^32. Any tau >= 0 gives the same result
+                            up to rounding; small values only cost extra passes. */
     int lpt_order;       /* 1 (default): heaviest query tiles first (longest-processing-
                             time-first, daily.dev "Summary"); 0: plain order. */
 } fa_fwd_options;

@@ -77,12 +77,13 @@ def test_forward_workload_sampled(name):
 
 
 def test_options_give_same_result():
-    """Conditional-rescale threshold, exp mode and tile order do not change the result."""
+    """Conditional-rescale threshold, exp mode and tile order do not change the result.
+    tau 0 and 8 send the workgroups through the tracking and exact passes, 32 does not."""
     x = I.make_inputs(1, 700, 4, 2, 128, True, seed=5)
     o_ref, lse_ref = H.oracle_forward(x)
     base = None
     for exp_mode in (capi.FA_EXP_HW, capi.FA_EXP_POLY):
-        for tau in (0.0, 8.0):
+        for tau in (0.0, 8.0, 32.0):
             for lpt in (0, 1):
                 opt = capi.FaOptions(exp_mode, tau, lpt)
                 *_, o, lse = H.gpu_forward(x, opt)
@@ -105,9 +106,11 @@ def test_rescale_events_forced():
     kf[:, 600] += 40.0 * np.sign(qf[:, 0:1, :, :])[:, 0]
     x.k = I.f32_to_bf16_bits(kf)
     o_ref, lse_ref = H.oracle_forward(x)
-    for tau in (0.0, 8.0):
-        *_, o, lse = H.gpu_forward(x, capi.FaOptions(capi.FA_EXP_HW, tau, 1))
-        H.check_forward(o, lse, o_ref, lse_ref, f"ramp tau={tau}")
+    # the spike outgrows the first tile's max by far more than the default
+    # tau, so every setting takes the exact re-run
+    for opt in (None, capi.FaOptions(capi.FA_EXP_HW, 0.0, 1), capi.FaOptions(capi.FA_EXP_HW, 8.0, 1)):
+        *_, o, lse = H.gpu_forward(x, opt)
+        H.check_forward(o, lse, o_ref, lse_ref, f"ramp {'default' if opt is None else opt.rescale_tau}")
 
 
 def test_large_scores_stay_finite():
