@@ -208,32 +208,58 @@ void bwd_dkdv_kernel(const BwdParams p) {
     }
   }
 
-  // ---- tile copies: tile `it` = (head gi, query tile qt), issued in order ----
+  // ---- tile copies: tile `it` = (head gi, query tile qt), issued in order.
+  // The sources of the next tile are kept as wave-uniform pointers: Q / dO
+  // rows and the LSE*log2(e) / D rows move TROWS rows on per tile and jump to
+  // the next query head's first tile after a head's last one (a few scalar
+  // adds per tile instead of recomputing 64-bit addresses). ----
   RC copy;
   copy.init(wave, lane, (unsigned)q_stride_b);
-  int iss_g = 0, iss_qt = qt0;
+  const int h_first = hkv * p.G;
+  const long tile_step = (long)TROWS * q_stride_b;                 // bytes per Q / dO tile
+  const long lse_head_step = VARLEN ? (long)T : (long)p.N;          // LSE elements between heads
+  const char* q_head = (const char*)p.q + ((long)seq0 * p.Hq + h_first) * D * 2 + qt0 * tile_step;
+  const char* o_head = (const char*)p.dout + ((long)seq0 * p.Hq + h_first) * D * 2 + qt0 * tile_step;
+  // LSE*log2(e) and D of the tile's rows: wave w moves rows (w & 1) * 32 + lane
+  // of array w >> 1 (lanes 0..31); rows of one (sequence, head) are contiguous
+  const float* l_head = (wave < 2 ? p.lse2 : p.dsum) +
+                        lse_index(p, s, h_first, seq0, qt0 * TROWS + (wave & 1) * 32, T, VARLEN);
+  q_head = uniform_ptr(q_head);
+  o_head = uniform_ptr(o_head);
+  l_head = uniform_ptr(l_head);
+  const char* q_cur = q_head;
+  const char* o_cur = o_head;
+  const float* l_cur = l_head;
+  int iss_qt = qt0;
   auto issue_next = [&](char FA_LDS* stage) __attribute__((always_inline)) {
-    const int h = hkv * p.G + iss_g;
     const int q0 = iss_qt * TROWS;
-    // LSE*log2(e) and D of the tile's rows: wave w moves rows (w & 1) * 32 + lane
-    // of array w >> 1 (lanes 0..31)
     if (lane < 32) {
-      // rows of one (sequence, head) are contiguous in the LSE layout
+      // rows past the sequence end repeat its last row (or, for a half tile
+      // wholly past it, fall outside the descriptor's range and read as 0)
       const int r0 = q0 + (wave & 1) * 32;
       const int r = min(r0 + lane, L - 1);
-      const float* src = (wave < 2 ? p.lse2 : p.dsum) + lse_index(p, s, h, seq0, r0, T, VARLEN);
-      buf2lds4(buffer_rsrc_uniform(src), (unsigned)(r - r0) * 4u,
+      buf2lds4(buffer_rsrc_uniform(l_cur), (unsigned)(r - r0) * 4u,
                stage + S::LSEOFF + (wave >> 1) * TROWS * 4 + (wave & 1) * 128);
     }
-    // (the compiler computes these addresses on the vector unit; the copies
-    // take them through readfirstlane)
-    const char* qb = (const char*)p.q + ((long)seq0 * p.Hq + h) * D * 2;
-    const char* ob = (const char*)p.dout + ((long)seq0 * p.Hq + h) * D * 2;
-    copy.template issue<true>(stage, qb, q_stride_b, q0, L);
-    copy.template issue<true>(stage + S::TILEB, ob, q_stride_b, q0, L);
+    if (q0 + TROWS <= L) {
+      copy.template issue_full<true>(stage, q_cur);
+      copy.template issue_full<true>(stage + S::TILEB, o_cur);
+    } else {
+      copy.template issue_tail<true>(stage, q_cur, q_stride_b, L - 1 - q0);
+      copy.template issue_tail<true>(stage + S::TILEB, o_cur, q_stride_b, L - 1 - q0);
+    }
     if (++iss_qt == n_qt) {
       iss_qt = qt0;
-      ++iss_g;
+      q_head = uniform_ptr(q_head + D * 2);
+      o_head = uniform_ptr(o_head + D * 2);
+      l_head = uniform_ptr(l_head + lse_head_step);
+      q_cur = q_head;
+      o_cur = o_head;
+      l_cur = l_head;
+    } else {
+      q_cur = uniform_ptr(q_cur + tile_step);
+      o_cur = uniform_ptr(o_cur + tile_step);
+      l_cur = uniform_ptr(l_cur + TROWS);
     }
   };
   issue_next(stg[0]);

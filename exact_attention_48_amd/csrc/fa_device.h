@@ -162,6 +162,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
   return buffer_rsrc((const void*)(((unsigned long long)hi << 32) | lo));
 }
+// A pointer that is equal in every lane, passed through readfirstlane so the
+// compiler keeps it (and what is computed from it) in scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const unsigned long long a = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return (T*)(((unsigned long long)hi << 32) | lo);
+}
 // `bytes` (4 or 16) per lane from rsrc + voffset into LDS: the 64 lanes fill
 // 64 * bytes of LDS starting at `lds` (wave-uniform), lane i at lds + bytes * i.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, void FA_LDS* lds) {
