@@ -389,7 +389,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
       if (e & 1) {
         // pair (e-1, e) -> positions of the B operand of key step t = qb*2 + (r/8)
         const int qb = e >> 4, r = e & 15;
-        pb[qb * 2 + (r >> 3)][(r & 7) >> 1] = __builtin_bit_cast(unsigned, pack_bf16(pf[e - 1], pf[e]));
+        unsigned w = __builtin_bit_cast(unsigned, pack_bf16(pf[e - 1], pf[e]));
+        asm volatile("" : "+v"(w));   // keep the pack in its MFMA slot (not sunk below the last MFMA)
+        pb[qb * 2 + (r >> 3)][(r & 7) >> 1] = w;
       }
     };
     auto step = [&](int t) __attribute__((always_inline)) {
