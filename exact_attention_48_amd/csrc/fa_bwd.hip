@@ -63,35 +63,59 @@ __device__ __forceinline__ long lse_index(const BwdParams& p, int s, int h, int 
 // ---------------------------------------------------------------------------
 // 1. D_i = sum_k dO[i,k] O[i,k]  and  LSE_i * log2(e)
 // ---------------------------------------------------------------------------
+// Block b takes query head b % Hq and the PREP_TOK consecutive tokens
+// (b / Hq) * PREP_TOK .. of the flattened (uniform: b * N + n) or packed token
+// axis. A row (token, head) of dO / O is D * 2 contiguous bytes, D / 8 lanes
+// load 16 bytes each, and every thread keeps the loads of all its rows in
+// flight; the block's LSE reads and D writes are then runs of consecutive
+// tokens of one head, contiguous within a sequence in the [B, Hq, N] / [Hq, T]
+// layout. Consecutive blocks take the heads of one token run, so the rows
+// they read lie side by side.
+constexpr int PREP_TOK = 64;
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, long total_rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, long n_tok) {
   constexpr int LPR = D / 8;                 // lanes per (token, head) row, 16 B each
-  constexpr int RPB = 256 / LPR;             // rows per block
-  const long r = (long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  long T = total_rows / p.Hq;
+  constexpr int RPP = 256 / LPR;             // rows per pass of the block
+  constexpr int PASSES = PREP_TOK / RPP;
+  static_assert(PASSES * RPP == PREP_TOK, "token run must split into whole passes");
+  const int h = (int)(blockIdx.x % (unsigned)p.Hq);
+  const long t0 = (long)(blockIdx.x / (unsigned)p.Hq) * PREP_TOK;
+  long T = n_tok;
   if constexpr (VARLEN) T = p.cu_seqlens[p.B];
-  const bool ok = r < T * p.Hq;
-  float acc = 0.f;
-  if (ok) {
-    const bf16x8 a = *(const bf16x8*)((const __bf16*)p.dout + r * D + part * 8);
-    const bf16x8 b = *(const bf16x8*)((const __bf16*)p.o + r * D + part * 8);
+  if (t0 >= T) return;
+  const int part = threadIdx.x % LPR;
+  const int sub = threadIdx.x / LPR;
+  bf16x8 a[PASSES], b[PASSES];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+  for (int u = 0; u < PASSES; ++u) {
+    const long t = t0 + u * RPP + sub;
+    if (t < T) {
+      const long off = (t * p.Hq + h) * D + part * 8;
+      a[u] = *(const bf16x8*)((const __bf16*)p.dout + off);
+      b[u] = *(const bf16x8*)((const __bf16*)p.o + off);
+    } else {
+      a[u] = bf16x8{};
+      b[u] = bf16x8{};
+    }
   }
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (ok && part == 0) {
-    const long t = r / p.Hq;
-    const int h = (int)(r - t * p.Hq);
-    long idx;
-    if constexpr (VARLEN) idx = (long)h * T + t;
-    else {
-      const long b = t / p.N, n = t - b * p.N;
-      idx = (b * p.Hq + h) * p.N + n;
+  for (int u = 0; u < PASSES; ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[u][e], (float)b[u][e], acc);
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    const long t = t0 + u * RPP + sub;
+    if (t < T && part == 0) {
+      long idx;
+      if constexpr (VARLEN) idx = (long)h * T + t;
+      else {
+        const long bt = t / p.N, n = t - bt * p.N;
+        idx = (bt * p.Hq + h) * p.N + n;
+      }
+      p.dsum[idx] = -acc;
+      p.lse2[idx] = p.lse[idx] * kLog2e;
     }
-    p.dsum[idx] = -acc;
-    p.lse2[idx] = p.lse[idx] * kLog2e;
   }
 }
 
@@ -811,10 +835,10 @@ template <int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_bwd_t(const BwdParams& p, int stages, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (stages & 1) {
-    const long rows = (long)p.B * p.N * p.Hq;    // upper bound (packed: T <= B * N)
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_prep_kernel<D, VARLEN>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       stream, p, rows);
+    const long n_tok = (long)p.B * p.N;          // upper bound (packed: T <= B * N)
+    const long grid = (n_tok + PREP_TOK - 1) / PREP_TOK * p.Hq;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_prep_kernel<D, VARLEN>), dim3((unsigned)grid), dim3(256), 0, stream, p, n_tok);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (VARLEN) {
       hipLaunchKernelGGL(bwd_sched_kernel, dim3(1), dim3(256), 0, stream, p.cu_seqlens, p.B, p.kv_chunks,
