@@ -31,23 +31,49 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const long b = bh / H;
   const long h = bh - b * H;
   const long orow = (b * N + n) * H + h;           // row of [B, N, H, d]
+  // LSE of the first PG parts stays in registers from the max pass, so for
+  // up to PG parts every weight is known before any O load goes out and all
+  // of a lane's loads are in flight together; more parts run in groups of PG.
+  // A part whose weight is 0 (its row saw no key of the chunk) loads nothing.
+  constexpr int PG = 16;
+  float lv[PG];
   float m = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) m = fmaxf(m, lse_part[p * rows + r]);
+#pragma unroll
+  for (int g = 0; g < PG; ++g) {
+    lv[g] = g < n_parts ? lse_part[g * rows + r] : -INFINITY;
+    m = fmaxf(m, lv[g]);
+  }
+  for (int p = PG; p < n_parts; ++p) m = fmaxf(m, lse_part[p * rows + r]);
   float acc[8] = {};
   float tot = 0.f;
   if (m != -INFINITY) {
-#pragma unroll 4
-    for (int p = 0; p < n_parts; ++p) {
-      const float w = expf(lse_part[p * rows + r] - m);
-      if (w > 0.f) {                               // a part whose row saw no key adds nothing
-        const float* src = o_part + (p * rows + orow) * D + col;
-        const f32x4 a = *(const f32x4*)src;
-        const f32x4 c = *(const f32x4*)(src + 4);
-        tot += w;
+    for (int p0 = 0; p0 < n_parts; p0 += PG) {
+      float w[PG];
+      f32x4 a[PG], c[PG];
+#pragma unroll
+      for (int g = 0; g < PG; ++g) {
+        const int p = p0 + g;
+        float l = lv[g];
+        if (p0 > 0) l = p < n_parts ? lse_part[p * rows + r] : -INFINITY;
+        w[g] = expf(l - m);
+      }
+#pragma unroll
+      for (int g = 0; g < PG; ++g) {
+        a[g] = f32x4{};
+        c[g] = f32x4{};
+        if (w[g] > 0.f) {
+          const float* src = o_part + ((p0 + g) * rows + orow) * D + col;
+          a[g] = *(const f32x4*)src;
+          c[g] = *(const f32x4*)(src + 4);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < PG; ++g) {
+        tot += w[g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[e] = __builtin_fmaf(w, a[e], acc[e]);
-          acc[4 + e] = __builtin_fmaf(w, c[e], acc[4 + e]);
+          acc[e] = __builtin_fmaf(w[g], a[g][e], acc[e]);
+          acc[4 + e] = __builtin_fmaf(w[g], c[g][e], acc[4 + e]);
         }
       }
     }
