@@ -29,7 +29,7 @@ FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_split",
-            "fa_merge",
+            "fa_merge", "fa_exp2_eval",
             "fa_status_string", "fa_version")
 
 
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_split.restype = ci
     lib.fa_merge.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
     lib.fa_merge.restype = ci
+    lib.fa_exp2_eval.argtypes = [vp, vp, ctypes.c_int64, ci, vp]
+    lib.fa_exp2_eval.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -167,6 +169,13 @@ def fa_merge(o_part, lse_part, o, lse, n_parts: int, B: int, H: int, N: int, d: 
                          _stream(stream))
     if check and st != FA_OK:
         raise FaError(st, "fa_merge")
+    return st
+
+
+def fa_exp2_eval(x, y, n: int, exp_mode: int, stream=None, check: bool = True) -> int:
+    st = load().fa_exp2_eval(_ptr(x), _ptr(y), int(n), int(exp_mode), _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_exp2_eval")
     return st
 
 

@@ -161,6 +161,14 @@ fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* l
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_exp2_eval(const float* x, float* y, int64_t n, int exp_mode, void* stream) {
+  if (n < 0 || (exp_mode != FA_EXP_HW && exp_mode != FA_EXP_POLY)) return FA_ERR_INVALID_ARGUMENT;
+  if (n == 0) return FA_OK;
+  if (!x || !y || !fa::aligned4(x) || !fa::aligned4(y)) return FA_ERR_INVALID_ARGUMENT;
+  hipError_t e = fa::exp2_eval_launch(x, y, (long)n, exp_mode, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int varlen) {
   return fa::bwd_workspace_bytes(B, Hq, Hkv, N, d, causal, varlen);
 }

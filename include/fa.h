@@ -213,6 +213,19 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
 fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                    int n_parts, int B, int H, int N, int d, void* stream);
 
+/*
+ * The element-wise exponential the softmax uses, on its own (a check of the
+ * kernels' software exponential with range reduction, phantomic12 summary,
+ * co-design list; daily.dev Summary): y[i] = 2^x[i] computed by the same
+ * device function as in fa_fwd / fa_bwd, FA_EXP_HW (v_exp_f32) or FA_EXP_POLY
+ * (exact split x = n + f, polynomial in f on the FMA pipe, n added to the
+ * exponent; inputs below -125 give 0).
+ *   x, y      fp32 [n], device, caller-owned, 4-byte aligned (may not overlap)
+ *   n         >= 0 (0 launches nothing)
+ * Returns FA_ERR_INVALID_ARGUMENT for n < 0, another mode or bad pointers.
+ */
+fa_status fa_exp2_eval(const float* x, float* y, int64_t n, int exp_mode, void* stream);
+
 /* Static, human-readable description of a status code. */
 const char* fa_status_string(fa_status s);
 

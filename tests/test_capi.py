@@ -171,3 +171,20 @@ def fp8(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128,
 ])
 def test_fp8_rejects(lib, kw, expect):
     assert fp8(**kw) == expect
+
+
+def exp2_eval(*, x=A, y=A + 4096, n=16, mode=capi.FA_EXP_HW):
+    return capi.fa_exp2_eval(x, y, n, mode, stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(mode=2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(mode=-1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(n=-1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(x=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(y=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(n=0), capi.FA_OK),
+    (dict(n=0, mode=capi.FA_EXP_POLY), capi.FA_OK),
+])
+def test_exp2_eval_rejects(lib, kw, expect):
+    assert exp2_eval(**kw) == expect
