@@ -4,6 +4,7 @@
 #include <cmath>
 
 #include "../../include/fa.h"
+#include "fa_exp2.h"
 #include "fa_kernels.h"
 #include "fa_validate.h"
 

@@ -10,7 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_device.h"
-#include "fa_kernels.h"
+#include "fa_exp2.h"
 
 namespace fa {
 
