@@ -28,9 +28,8 @@ FA_BWD_DKDV = 2
 FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_split",
-            "fa_merge", "fa_exp2_eval",
-            "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_fp8_ex",
+            "fa_fwd_split", "fa_fwd_split_ex", "fa_merge", "fa_exp2_eval", "fa_status_string", "fa_version")
 
 
 class FaOptions(ctypes.Structure):
@@ -69,8 +68,13 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_ex.restype = ci
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp]
     lib.fa_fwd_fp8.restype = ci
+    lib.fa_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp,
+                                  ctypes.POINTER(FaOptions), vp]
+    lib.fa_fwd_fp8_ex.restype = ci
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.fa_fwd_split.restype = ci
+    lib.fa_fwd_split_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ctypes.POINTER(FaOptions), vp]
+    lib.fa_fwd_split_ex.restype = ci
     lib.fa_merge.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
     lib.fa_merge.restype = ci
     lib.fa_exp2_eval.argtypes = [vp, vp, ctypes.c_int64, ci, vp]
@@ -163,6 +167,17 @@ def fa_fwd_split(q, k, v, o_part, lse_part, B: int, Hq: int, Hkv: int, Nq: int, 
     return st
 
 
+def fa_fwd_split_ex(q, k, v, o_part, lse_part, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, causal: int,
+                    softmax_scale: float, n_splits: int, options: Optional[FaOptions] = None, stream=None,
+                    check: bool = True) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    st = load().fa_fwd_split_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, Hq, Hkv, Nq, Nk, d,
+                                int(causal), float(softmax_scale), int(n_splits), opt, _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_fwd_split_ex")
+    return st
+
+
 def fa_merge(o_part, lse_part, o, lse, n_parts: int, B: int, H: int, N: int, d: int, stream=None,
              check: bool = True) -> int:
     st = load().fa_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), int(n_parts), B, H, N, d,
@@ -185,4 +200,16 @@ def fa_fwd_fp8(q8, k8, v, q_descale, k_descale, o, lse, B: int, Hq: int, Hkv: in
                            Hq, Hkv, N, d, int(causal), float(softmax_scale), _ptr(cu_seqlens), _stream(stream))
     if check and st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
+    return st
+
+
+def fa_fwd_fp8_ex(q8, k8, v, q_descale, k_descale, o, lse, B: int, Hq: int, Hkv: int, N: int, d: int, causal: int,
+                  softmax_scale: float, cu_seqlens=None, options: Optional[FaOptions] = None, stream=None,
+                  check: bool = True) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    st = load().fa_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(o), _ptr(lse),
+                              B, Hq, Hkv, N, d, int(causal), float(softmax_scale), _ptr(cu_seqlens), opt,
+                              _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8_ex")
     return st

@@ -94,11 +94,12 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, nullptr, stream);
 }
 
-fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
-                     void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
-                     const int32_t* cu_seqlens, void* stream) {
+fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float softmax_scale, const int32_t* cu_seqlens,
+                        const fa_fwd_options* options, void* stream) {
   const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
-  fa_status st = fa::check_fp8(q, k, v, q_descale, k_descale, o, lse, pr, softmax_scale, cu_seqlens);
+  fa_status st = fa::check_fp8(q, k, v, q_descale, k_descale, o, lse, pr, softmax_scale, cu_seqlens, options);
   if (st != FA_OK) return st;
   if (fa::empty_problem(pr)) return FA_OK;
   fa::FwdParams p{};
@@ -113,21 +114,28 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
   p.N = N;
-  p.lpt = 1;
+  p.lpt = options ? options->lpt_order : 1;
   p.kv_chunks = fa::xcd_chunks(Hkv);
   p.scale_log2 = softmax_scale * kLog2eF;
-  p.tau = kDefaultTau;
+  p.tau = options ? options->rescale_tau : kDefaultTau;
   p.q_descale = q_descale;
   p.k_descale = k_descale;
   hipError_t e = fa::fwd_fp8_launch(p, causal, cu_seqlens != nullptr, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
-                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
-                       int n_splits, void* stream) {
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                     const int32_t* cu_seqlens, void* stream) {
+  return fa_fwd_fp8_ex(q, k, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens,
+                       nullptr, stream);
+}
+
+fa_status fa_fwd_split_ex(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                          int n_splits, const fa_fwd_options* options, void* stream) {
   fa_status st = fa::check_split(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale,
-                                 n_splits);
+                                 n_splits, options);
   if (st != FA_OK) return st;
   if (B == 0 || Nq == 0) return FA_OK;
   fa::FwdParams p{};
@@ -139,10 +147,10 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
   p.N = Nq;
-  p.lpt = 1;
+  p.lpt = options ? options->lpt_order : 1;
   p.kv_chunks = fa::xcd_chunks(Hkv);
   p.scale_log2 = softmax_scale * kLog2eF;
-  p.tau = kDefaultTau;
+  p.tau = options ? options->rescale_tau : kDefaultTau;
   p.o_part = o_part;
   p.lse_part = lse_part;
   p.Nk = Nk;
@@ -151,6 +159,13 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
   p.chunk = (Nk + n_splits - 1) / n_splits;
   hipError_t e = fa::fwd_split_launch(p, d, causal, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                       int n_splits, void* stream) {
+  return fa_fwd_split_ex(q, k, v, o_part, lse_part, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale, n_splits,
+                         nullptr, stream);
 }
 
 fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B, int H,

@@ -32,11 +32,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// The same MFMA with the register file of each operand fixed by inline asm
+// v_mfma_f32_32x32x16_bf16 with the register file of each operand fixed by inline asm
 // (the compiler would otherwise put every accumulator in AGPRs and copy the
 // ones the VALU reads back every tile). The compiler does not see these as
 // MFMAs, so their users keep the hazard rules themselves: a VALU write of an
@@ -66,25 +62,6 @@ __device__ __forceinline__ void mfma8_v_first(f32x16& acc, const i32x8& a, const
 }
 __device__ __forceinline__ void mfma8_v(f32x16& acc, const i32x8& a, const i32x8& b) {
   asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-// acc *= alpha for an accumulator held in AGPRs, in place (each register read
-// to a VGPR, multiplied, written back), so that the compiler never moves the
-// accumulator out of the AGPRs for VALU arithmetic. Callers wait for the
-// MFMAs that wrote `acc` first (mfma_result_wait).
-__device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
-  float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3], e4 = acc[4], e5 = acc[5], e6 = acc[6], e7 = acc[7];
-  float e8 = acc[8], e9 = acc[9], e10 = acc[10], e11 = acc[11], e12 = acc[12], e13 = acc[13], e14 = acc[14],
-        e15 = acc[15];
-  float t;
-#define FA_SCALE1(i) "v_accvgpr_read_b32 %16, %" #i "\n v_mul_f32 %16, %16, %17\n v_accvgpr_write_b32 %" #i ", %16\n"
-  asm volatile(FA_SCALE1(0) FA_SCALE1(1) FA_SCALE1(2) FA_SCALE1(3) FA_SCALE1(4) FA_SCALE1(5) FA_SCALE1(6)
-                   FA_SCALE1(7) FA_SCALE1(8) FA_SCALE1(9) FA_SCALE1(10) FA_SCALE1(11) FA_SCALE1(12) FA_SCALE1(13)
-                       FA_SCALE1(14) FA_SCALE1(15)
-               : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "+a"(e4), "+a"(e5), "+a"(e6), "+a"(e7), "+a"(e8),
-                 "+a"(e9), "+a"(e10), "+a"(e11), "+a"(e12), "+a"(e13), "+a"(e14), "+a"(e15), "=&v"(t)
-               : "v"(alpha));
-#undef FA_SCALE1
-  acc = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
 }
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory"); }
 // Keeps an asm MFMA result allocated up to this point (a result that is never
@@ -185,11 +162,6 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // s_waitcnt immediate: at most `vm` vector-memory operations (which include the
 // HBM->LDS copies) and no LDS operation of this wave outstanding.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
-// vmcnt <= vm and lgkmcnt <= lgkm (lgkm <= 15; 15 does not wait on LDS at all)
-constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
-  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
-}
-
 // Workgroup barrier WITHOUT the memory fence of __syncthreads(): that fence
 // waits for every outstanding vector-memory operation, i.e. it would drain the
 // HBM->LDS copies still in flight for later tiles. Callers wait explicitly for
@@ -199,19 +171,27 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 
 // exp2 on the FMA pipe: exact split x = n + f with n = floor(x), f in [0, 1),
 // 2^f from a minimax polynomial (coefficients fitted by gen_exp2_poly.py),
-// 2^n applied by adding n to the exponent field. Inputs below -125 return 0
-// (so a masked -inf gives exactly 0 and no result is denormal: p(f) may be
-// slightly below 1, which would push 2^-126 p(f) out of the normal range).
+// 2^n applied by v_ldexp_f32. Range handling:
+//   x < -125   -> 0 (a masked -inf gives exactly 0, and no result is denormal:
+//                 p(f) may be slightly below 1, which would push 2^-126 p(f)
+//                 out of the normal range);
+//   x >= 128   -> +inf (2^128 is past the float32 range; selected at the end,
+//                 since p(0) is slightly below 1);
+//   NaN        -> NaN (the clamp is a select, which keeps a NaN where fmaxf
+//                 would replace it by the bound, and (int)NaN is 0 on
+//                 v_cvt_i32_f32, so v_ldexp_f32 returns the NaN).
 #include "exp2_poly_coeffs.h"
 __device__ __forceinline__ float exp2_poly(float x) {
-  const float xc = fmaxf(x, -125.0f);
+  const bool under = x < -125.0f;
+  const float xc = under ? -125.0f : x;
   const float n = __builtin_floorf(xc);
   const float f = xc - n;
   float p = kExp2Poly[kExp2PolyDegree];
 #pragma unroll
   for (int i = kExp2PolyDegree - 1; i >= 0; --i) p = __builtin_fmaf(p, f, kExp2Poly[i]);
-  const int bits = __float_as_int(p) + ((int)n << 23);
-  return x < -125.0f ? 0.0f : __int_as_float(bits);
+  float r = __builtin_amdgcn_ldexpf(p, (int)n);
+  r = x >= 128.0f ? __builtin_inff() : r;
+  return under ? 0.0f : r;
 }
 
 // XOR swizzle of the 16-byte chunks of row `row` of a bf16 [rows][D] tile in

@@ -570,8 +570,6 @@ static hipError_t launch_fwd_d(const FwdParams& p, int grid, int causal, int var
                 : launch_fwd_e<D, false, false>(p, grid, expmode, stream);
 }
 
-int fwd_block_m() { return BM; }
-
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream) {
   p.n_qtiles = (p.N + BM - 1) / BM;
   const long grid_l = varlen ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles)

@@ -36,7 +36,6 @@ hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream);
 hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, hipStream_t stream);
 hipError_t merge_launch(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B,
                         int H, int N, int d, hipStream_t stream);
-int fwd_block_m();
 
 struct BwdParams {
   const void* q;

@@ -188,23 +188,5 @@ __device__ __forceinline__ void wait_vm(int n) {
 #undef FA_WAIT_CASE
 }
 
-// As wait_vm, but up to `lgkm` LDS operations (the newest ones; LDS
-// operations of a wave complete in order) may stay outstanding; both counts
-// must be compile-time constants after inlining (vm <= 20, lgkm <= 15).
-template <int LGKM>
-__device__ __forceinline__ void wait_vm_lgkm(int n) {
-  static_assert(LGKM >= 0 && LGKM <= 15, "lgkmcnt is a 4-bit field");
-#define FA_WAIT_CASE(k) \
-  case k: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(k, LGKM)); break;
-  switch (n) {
-    FA_WAIT_CASE(0) FA_WAIT_CASE(1) FA_WAIT_CASE(2) FA_WAIT_CASE(3) FA_WAIT_CASE(4) FA_WAIT_CASE(5)
-    FA_WAIT_CASE(6) FA_WAIT_CASE(7) FA_WAIT_CASE(8) FA_WAIT_CASE(9) FA_WAIT_CASE(10)
-    FA_WAIT_CASE(11) FA_WAIT_CASE(12) FA_WAIT_CASE(13) FA_WAIT_CASE(14) FA_WAIT_CASE(15)
-    FA_WAIT_CASE(16) FA_WAIT_CASE(17) FA_WAIT_CASE(18) FA_WAIT_CASE(19) FA_WAIT_CASE(20)
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, LGKM)); break;
-  }
-#undef FA_WAIT_CASE
-}
-
 }  // namespace tiles
 }  // namespace fa

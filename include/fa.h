@@ -52,7 +52,8 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, Hq % Hkv != 0, non-finite scale */
+    FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, Hq % Hkv != 0, scale not
+                                    finite or negative */
     FA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head size other than 64 or 128) */
     FA_ERR_WORKSPACE = 3,        /* backward workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
@@ -90,7 +91,10 @@ typedef struct {
  *   N            sequence length (uniform) or maximum sequence length (packed); N >= 0
  *   d            head size (64 or 128)
  *   causal       0 or 1
- *   softmax_scale finite scale applied to Q K^T
+ *   softmax_scale finite scale >= 0 applied to Q K^T (the kernels take the row maxima of
+ *                the raw products Q K^T and fold the scale into the exponent, which is
+ *                exact only for a non-negative scale; a negative one returns
+ *                FA_ERR_INVALID_ARGUMENT)
  *   cu_seqlens   NULL (uniform) or device int32[B+1] (packed)
  *   stream       hipStream_t or NULL
  * B == 0 or N == 0 is a valid empty call and enqueues nothing.
@@ -170,6 +174,16 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q
                      const int32_t* cu_seqlens, void* stream);
 
 /*
+ * fa_fwd_fp8 with explicit options (NULL = defaults). rescale_tau and lpt_order
+ * act as for fa_fwd_ex; exp_mode must be FA_EXP_HW (FA_EXP_POLY returns
+ * FA_ERR_UNSUPPORTED for the 8-bit kernel).
+ */
+fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float softmax_scale, const int32_t* cu_seqlens,
+                        const fa_fwd_options* options, void* stream);
+
+/*
  * Split-KV partial attention (uniform batches). The keys of every sequence are
  * cut into n_splits contiguous chunks of C = ceil(Nk / n_splits) keys (chunk p:
  * keys p*C .. min((p+1)*C, Nk) - 1; chunks past the end are empty). For every
@@ -197,6 +211,15 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, float* o_par
                        int n_splits, void* stream);
 
 /*
+ * fa_fwd_split with explicit options (NULL = defaults). rescale_tau and
+ * lpt_order act as for fa_fwd_ex; exp_mode must be FA_EXP_HW (FA_EXP_POLY
+ * returns FA_ERR_UNSUPPORTED for the split kernel).
+ */
+fa_status fa_fwd_split_ex(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale,
+                          int n_splits, const fa_fwd_options* options, void* stream);
+
+/*
  * Merge of partial attention results (the combination step of the online
  * softmax, podcast.app episode page, description), row by row:
  *   LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
@@ -217,9 +240,11 @@ fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* l
  * The element-wise exponential the softmax uses, on its own (a check of the
  * kernels' software exponential with range reduction, phantomic12 summary,
  * co-design list; daily.dev Summary): y[i] = 2^x[i] computed by the same
- * device function as in fa_fwd / fa_bwd, FA_EXP_HW (v_exp_f32) or FA_EXP_POLY
- * (exact split x = n + f, polynomial in f on the FMA pipe, n added to the
- * exponent; inputs below -125 give 0).
+ * device function as the forward pass selects with fa_fwd_options.exp_mode,
+ * FA_EXP_HW (v_exp_f32) or FA_EXP_POLY (exact split x = n + f, polynomial in f
+ * on the FMA pipe, 2^n applied by v_ldexp_f32; inputs below -125 give 0,
+ * inputs at or above 128 give +inf, NaN stays NaN). The backward pass always
+ * uses v_exp_f32.
  *   x, y      fp32 [n], device, caller-owned, 4-byte aligned (may not overlap)
  *   n         >= 0 (0 launches nothing)
  * Returns FA_ERR_INVALID_ARGUMENT for n < 0, another mode or bad pointers.

@@ -62,9 +62,39 @@ def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
 
 
-def sampled_rows(n_first=128, n_last=128, stride=97):
-    """Row selector for long sequences: first and last rows plus a strided sample."""
+
+
+def block_rows(n_first=64, n_last=64, block=32):
+    """Row selector for full-size sequences: the first and the last row of every
+    32-row block (the rows of one MFMA query block; every wave of every query
+    tile holds whole blocks), plus the first and last rows of the sequence."""
     def sel(s, L):
-        r = set(range(min(n_first, L))) | set(range(max(0, L - n_last), L)) | set(range(0, L, stride))
-        return np.array(sorted(r), dtype=np.int64)
+        r = np.arange(L, dtype=np.int64)
+        keep = (r % block == 0) | (r % block == block - 1) | (r < n_first) | (r >= L - n_last)
+        return r[keep]
     return sel
+
+
+def wave_coverage(rows: np.ndarray, L: int, tile: int = 256, wave_rows: int = 32) -> np.ndarray:
+    """Compared rows per (query tile, wave slot) for `wave_rows`-row waves of `tile`-row
+    workgroups; asserts that every slot holding rows of the sequence has at least two."""
+    n_t = (L + tile - 1) // tile
+    counts = np.zeros((n_t, tile // wave_rows), dtype=np.int64)
+    np.add.at(counts, (rows // tile, (rows % tile) // wave_rows), 1)
+    starts = np.arange(n_t)[:, None] * tile + np.arange(tile // wave_rows)[None, :] * wave_rows
+    live = starts < L
+    assert np.all(counts[live] >= min(2, wave_rows)), "a wave slot of some query tile has no compared row"
+    return counts
+
+
+def poisoned(shape, dtype, guard: int = 4096):
+    """A NaN-filled device buffer with `guard` extra NaN elements after the view."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + guard,), float("nan"), dtype=dtype, device="cuda:0")
+    return buf[:n].view(shape), buf
+
+
+def assert_fully_written(view: torch.Tensor, buf: torch.Tensor, label: str):
+    n = view.numel()
+    assert not torch.isnan(view).any(), f"{label}: some element was not written"
+    assert torch.isnan(buf[n:]).all(), f"{label}: write past the end"

@@ -490,3 +490,33 @@ def pin_fp8(fwd8, decode):
             ob, lb = bruteforce.forward(qf.tolist(), kf.tolist(), v.tolist(), scale, causal, cu.tolist())
         assert np.max(np.abs(o - np.array(ob))) < TOL, ("FP8 O vs brute force", B, N, causal, lens)
         assert np.max(np.abs(lse - np.array(lb))) < TOL, ("FP8 LSE vs brute force", B, N, causal, lens)
+
+
+def pin_rowdot(rowdot):
+    """D_i = dO_i . O_i equals sum_j P_ij dP_ij with dP_ij = dO_i . V_j (O_i = sum_j P_ij V_j):
+    P and O from the pure-Python brute force, the double sum in math.fsum, for uniform and
+    packed layouts ([B, Hq, N] and [Hq, T]), causal, with grouped K/V heads."""
+    from oracle import bruteforce as bf
+    rng = np.random.default_rng(4)
+    for cu in (None, np.array([0, 3, 3, 7], dtype=np.int32)):
+        shp_q, shp_k = ((2, 5, 4, 3), (2, 5, 2, 3)) if cu is None else ((7, 4, 3), (7, 2, 3))
+        q, k, v = rng.standard_normal(shp_q), rng.standard_normal(shp_k), rng.standard_normal(shp_k)
+        do = rng.standard_normal(shp_q)
+        o, _ = bf.forward(q.tolist(), k.tolist(), v.tolist(), 0.7, True, None if cu is None else cu.tolist())
+        o = np.array(o)
+        d = rowdot(do, o)
+        seqs = [(b, b, 5) for b in range(2)] if cu is None else [(s, int(cu[s]), int(cu[s + 1] - cu[s])) for s in range(3)]
+        for s, start, L in seqs:
+            for h in range(4):
+                g = h // 2
+                for i in range(L):
+                    row = (lambda x, j: x[s, j, h]) if cu is None else (lambda x, j: x[start + j, h])
+                    krow = (lambda x, j: x[s, j, g]) if cu is None else (lambda x, j: x[start + j, g])
+                    sc = [0.7 * math.fsum(a * b for a, b in zip(row(q, i), krow(k, j))) for j in range(i + 1)]
+                    m = max(sc)
+                    e = [math.exp(x - m) for x in sc]
+                    z = math.fsum(e)
+                    dp = [math.fsum(a * b for a, b in zip(row(do, i), krow(v, j))) for j in range(i + 1)]
+                    want = math.fsum(e[j] / z * dp[j] for j in range(i + 1))
+                    got = d[s, h, i] if cu is None else d[h, start + i]
+                    assert abs(got - want) <= 1e-12 * (1 + abs(want)), (cu is None, s, h, i, got, want)

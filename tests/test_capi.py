@@ -62,6 +62,8 @@ def fwd(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, s
     (dict(causal=2), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.1), capi.FA_ERR_INVALID_ARGUMENT),          # row maxima are taken on the raw Q K^T
+    (dict(scale=-1e-30), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(q=A + 8), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(o=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(lse=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
@@ -99,6 +101,7 @@ def bwd(*, ws=A, ws_bytes=1 << 30, stages=capi.FA_BWD_ALL, **kw):
     (dict(Hq=4, Hkv=3), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(stages=0), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(stages=8), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.1), capi.FA_ERR_INVALID_ARGUMENT),
 ])
 def test_backward_rejects(lib, kw, expect):
     assert bwd(**kw) == expect
@@ -112,7 +115,10 @@ def test_workspace_size(lib):
     assert n >= 2 * 3 * 7 * 5 * 4 and n % 256 == 0
 
 
-def split(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, Nq=16, Nk=64, d=128, causal=1, scale=0.1, n=4):
+def split(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, Nq=16, Nk=64, d=128, causal=1, scale=0.1, n=4, opt=None):
+    if opt is not None:
+        return capi.fa_fwd_split_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, n, opt, stream=0,
+                                    check=False)
     return capi.fa_fwd_split(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, n, stream=0, check=False)
 
 
@@ -128,6 +134,10 @@ def split(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, Nq=16, Nk=64, d=128, c
     (dict(o=A + 4), capi.FA_ERR_INVALID_ARGUMENT),            # fp32 partial rows need 16-byte alignment
     (dict(causal=2), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(scale=math.nan), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.5), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(capi.FA_EXP_POLY, 8.0, 1)), capi.FA_ERR_UNSUPPORTED),   # split kernel: v_exp_f32
+    (dict(opt=capi.FaOptions(0, 65.0, 1)), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(0, 8.0, 1), B=0), capi.FA_OK),
     (dict(B=0), capi.FA_OK),                                   # empty: nothing to do
     (dict(Nq=0), capi.FA_OK),
 ])
@@ -155,7 +165,11 @@ def test_merge_rejects(lib, kw, expect):
     assert merge(**kw) == expect
 
 
-def fp8(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, scale=0.1, cu=None):
+def fp8(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, scale=0.1, cu=None,
+        opt=None):
+    if opt is not None:
+        return capi.fa_fwd_fp8_ex(q, k, v, qd, kd, o, lse, B, Hq, Hkv, N, d, causal, scale, cu, opt, stream=0,
+                                  check=False)
     return capi.fa_fwd_fp8(q, k, v, qd, kd, o, lse, B, Hq, Hkv, N, d, causal, scale, cu, stream=0, check=False)
 
 
@@ -167,6 +181,10 @@ def fp8(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128,
     (dict(q=None), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(Hq=3, Hkv=2), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(causal=3), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.1), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(capi.FA_EXP_POLY, 8.0, 1)), capi.FA_ERR_UNSUPPORTED),   # 8-bit kernel: v_exp_f32
+    (dict(opt=capi.FaOptions(0, 8.0, 3)), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(0, 8.0, 0), B=0), capi.FA_OK),
     (dict(B=0), capi.FA_OK),
 ])
 def test_fp8_rejects(lib, kw, expect):

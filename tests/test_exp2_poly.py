@@ -5,7 +5,8 @@ x = n + f, n = floor(x), evaluates the fitted polynomial at f with FMAs and
 adds n to the exponent field. This test evaluates the same steps in float32
 (FMA emulated exactly through float64) over a dense grid and compares with
 numpy's exp2 in float64; the GPU path itself is exercised end to end by the
-FA_EXP_POLY parity tests.
+FA_EXP_POLY parity tests. Out-of-range inputs: x < -125 gives 0, x >= 128
+gives +inf (2^128 is past the float32 range), and NaN stays NaN.
 """
 import os
 import re
@@ -34,15 +35,20 @@ def fma32(a, b, c):
 def exp2_poly_emulated(x):
     c, _ = coeffs()
     x = x.astype(np.float32)
-    xc = np.maximum(x, np.float32(-125.0))
-    n = np.floor(xc)
-    f = (xc - n).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        under = x < np.float32(-125.0)
+        xc = np.where(under, np.float32(-125.0), x)          # a select: a NaN stays NaN
+        n = np.floor(xc)
+        f = (xc - n).astype(np.float32)
     p = np.full_like(f, c[-1])
     for ci in c[-2::-1]:
         p = fma32(p, f, np.full_like(f, ci))
-    bits = p.view(np.int32) + (n.astype(np.int32) << 23)
-    out = bits.view(np.float32)
-    return np.where(x < -125.0, np.float32(0.0), out)
+    ni = np.where(np.isfinite(n), np.clip(n, -(2 ** 31), 2 ** 31 - 1), 0).astype(np.int64)
+    ni = np.clip(ni, -1000, 1000).astype(np.int32)            # v_ldexp_f32 saturates the same way
+    with np.errstate(over="ignore", invalid="ignore"):
+        out = np.ldexp(p, ni).astype(np.float32)
+        out = np.where(x >= np.float32(128.0), np.float32(np.inf), out)
+    return np.where(under, np.float32(0.0), out)
 
 
 def test_relative_error_within_fit_bound():
@@ -58,6 +64,21 @@ def test_relative_error_within_fit_bound():
 def test_masked_and_tiny_inputs_give_zero():
     x = np.array([-np.inf, -1000.0, -127.0, -125.5], dtype=np.float32)
     assert np.all(exp2_poly_emulated(x) == 0.0)
+
+
+def test_overflow_and_nan():
+    """Inputs at and above 128 overflow to +inf, as 2^x does in float32; the largest
+    finite results stay finite; NaN is passed through (so a non-finite row sum in
+    the forward pass still triggers its re-run)."""
+    x = np.array([127.0, 127.99, 128.0, 129.5, 140.0, 200.0, 520.0, np.inf, np.nan], dtype=np.float32)
+    y = exp2_poly_emulated(x)
+    assert np.all(np.isfinite(y[:2])) and y[0] == np.float32(2.0 ** 127) * np.float32(coeffs()[0][0])
+    assert np.all(y[2:8] == np.inf), y
+    assert np.isnan(y[8])
+    grid = np.linspace(100.0, 600.0, 20001, dtype=np.float32)
+    g = exp2_poly_emulated(grid)
+    assert np.all(np.isfinite(g[grid < 128.0])) and np.all(g[grid >= 128.0] == np.inf)
+    assert np.all(np.diff(g[grid < 128.0]) >= 0)
 
 
 def test_integers_are_near_exact():

@@ -26,8 +26,10 @@ def sample():
     ints = np.arange(-130, 1, dtype=np.float32)
     near_ints = np.concatenate([ints + np.float32(2.0 ** -20), ints - np.float32(2.0 ** -20)])
     tiny = np.float32(-1.0) * np.logspace(-30, 0, 4096, dtype=np.float64).astype(np.float32)
-    special = np.array([0.0, -0.0, -np.inf, -125.0, -125.5, -126.0, -127.0, -1000.0, 1.0, 7.5], dtype=np.float32)
-    return np.concatenate([grid, ints, near_ints, tiny, special]).astype(np.float32)
+    special = np.array([0.0, -0.0, -np.inf, -125.0, -125.5, -126.0, -127.0, -1000.0, 1.0, 7.5, 127.0, 127.99,
+                        128.0, 140.0, 200.0, 520.0, np.inf], dtype=np.float32)
+    high = rng.uniform(100.0, 600.0, size=1 << 14).astype(np.float32)     # up to and past overflow
+    return np.concatenate([grid, ints, near_ints, tiny, special, high]).astype(np.float32)
 
 
 def run(x, mode):
@@ -48,12 +50,15 @@ def test_polynomial_matches_host_emulation():
     x = sample()
     got = run(x, capi.FA_EXP_POLY)
     want = exp2_poly_emulated(x)
+    assert np.all(got[x >= 128.0] == np.inf), "2^x for x >= 128 must overflow to +inf"
+    nan_in = np.array([np.nan, -np.nan], dtype=np.float32)
+    assert np.all(np.isnan(run(nan_in, capi.FA_EXP_POLY))), "NaN must stay NaN"
     d = ulp_diff(got, want)
     assert np.max(d) <= 1, (np.max(d), x[np.argmax(d)])
     exact = np.mean(d == 0)
     assert exact >= 0.999, exact
     _, bound = coeffs()
-    ok = x >= -125.0
+    ok = (x >= -125.0) & (x < 127.0)
     ref = np.exp2(x[ok].astype(np.float64))
     rel = np.max(np.abs(got[ok].astype(np.float64) / ref - 1.0))
     assert rel <= bound + 2.5e-7, rel
@@ -63,7 +68,7 @@ def test_polynomial_matches_host_emulation():
 def test_hardware_exp_error_measured():
     x = sample()
     got = run(x, capi.FA_EXP_HW)
-    normal = (x >= -126.0) & np.isfinite(x)
+    normal = (x >= -126.0) & (x < 127.0)
     ref = np.exp2(x[normal].astype(np.float64))
     rel = np.abs(got[normal].astype(np.float64) / ref - 1.0)
     worst = float(np.max(rel))
@@ -71,3 +76,4 @@ def test_hardware_exp_error_measured():
     assert worst <= 2.0 ** -21, worst               # a few ulp: far below the bf16 rounding of P (2^-9)
     assert got[x == -np.inf][0] == 0.0
     assert got[x == 0.0][0] == 1.0
+    assert np.all(got[x >= 128.0] == np.inf)

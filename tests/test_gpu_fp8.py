@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_48_amd import inputs as I, ops
+from exact_attention_48_amd import capi, inputs as I, ops
 from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -19,11 +19,11 @@ def _dev8(codes):
     return torch.from_numpy(np.ascontiguousarray(codes)).to("cuda:0")
 
 
-def _run(x: I.Fp8Inputs):
+def _run(x: I.Fp8Inputs, options=None):
     cu = torch.from_numpy(x.cu_seqlens).to("cuda:0") if x.cu_seqlens is not None else None
     o, lse = ops.forward_fp8(_dev8(x.q8), _dev8(x.k8), H.dev(x.v), torch.from_numpy(x.q_descale).cuda(),
                              torch.from_numpy(x.k_descale).cuda(), x.causal, x.scale, cu,
-                             x.N if cu is not None else None)
+                             x.N if cu is not None else None, options=options)
     torch.cuda.synchronize()
     return o, lse
 
@@ -63,9 +63,28 @@ def test_fp8_descales_are_per_sequence_and_head():
 
 
 def test_fp8_workload_sampled():
-    """fp8_fwd_b4_h16_n4096_d128 at full size (the bench's launch): sampled rows against the oracle."""
+    """fp8_fwd_b4_h16_n4096_d128 at full size (the bench's launch): the first and last row of every
+    32-row query block of every (batch, head) against the oracle, so every wave of every tile."""
     w = I.WORKLOADS["fp8_fwd_b4_h16_n4096_d128"]
     x = I.workload_inputs(w.name)
     o, lse = _run(x)
-    o_ref, lse_ref = _oracle(x, rows=H.sampled_rows(64, 64, 509))
+    rows = H.block_rows()
+    cov = H.wave_coverage(rows(0, x.N), x.N).sum(axis=0)
+    print(f"{w.name}: compared rows per wave slot (summed over tiles): {cov.tolist()}")
+    o_ref, lse_ref = _oracle(x, rows=rows)
     H.check_forward(o, lse, o_ref, lse_ref, w.name)
+
+
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_fp8_forced_rescale(tau):
+    """Scores rising along the key axis and a late spike: tau 0 and 8 send the 8-bit kernel's
+    workgroups through the tracking and exact passes; the result matches the oracle."""
+    x = I.make_fp8_inputs(1, 640, 2, 2, 128, False, seed=430)
+    k = oracle.e4m3_to_float(x.k8).astype(np.float32) * x.k_descale[0][None, None, :, None]
+    q = oracle.e4m3_to_float(x.q8).astype(np.float32) * x.q_descale[0][None, None, :, None]
+    k = k + np.linspace(0, 6, 640, dtype=np.float32)[None, :, None, None] * np.sign(q.mean(axis=1, keepdims=True))
+    k[:, 600] += 40.0 * np.sign(q[:, 0])
+    x.k8, x.k_descale = I._quantize_heads(k, None, 1)
+    o_ref, lse_ref = _oracle(x)
+    o, lse = _run(x, capi.FaOptions(capi.FA_EXP_HW, tau, 1))
+    H.check_forward(o, lse, o_ref, lse_ref, f"fp8 forced rescale tau={tau}")

@@ -68,10 +68,15 @@ def test_forward_workload_small_d64():
 @pytest.mark.parametrize("name", ["fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
                                   "fwd_causal_varlen16_hq32_hkv8_d128", "fwd_causal_b1_h16_n131072_d128"])
 def test_forward_workload_sampled(name):
-    """Full-size workloads, checked on sampled rows of every (sequence, head)."""
+    """Full-size workloads with the launch the bench times, checked on every (sequence, head) at
+    the first and last row of every 32-row query block, so that every wave of every query
+    tile is compared (the per-wave-slot counts are printed and asserted)."""
     x = I.workload_inputs(name)
     *_, o, lse = H.gpu_forward(x)
-    rows = H.sampled_rows(n_first=64, n_last=64, stride=509)
+    rows = H.block_rows()
+    lens = np.diff(x.cu_seqlens) if x.cu_seqlens is not None else [x.N] * x.B
+    cov = sum(H.wave_coverage(rows(0, int(L)), int(L)).sum(axis=0) for L in lens if L > 0)
+    print(f"{name}: compared rows per wave slot (summed over tiles and sequences): {cov.tolist()}")
     o_ref, lse_ref = H.oracle_forward(x, rows=rows)
     H.check_forward(o, lse, o_ref, lse_ref, name)
 
@@ -108,9 +113,29 @@ def test_rescale_events_forced():
     o_ref, lse_ref = H.oracle_forward(x)
     # the spike outgrows the first tile's max by far more than the default
     # tau, so every setting takes the exact re-run
-    for opt in (None, capi.FaOptions(capi.FA_EXP_HW, 0.0, 1), capi.FaOptions(capi.FA_EXP_HW, 8.0, 1)):
+    for opt in (None, capi.FaOptions(capi.FA_EXP_HW, 0.0, 1), capi.FaOptions(capi.FA_EXP_HW, 8.0, 1),
+                capi.FaOptions(capi.FA_EXP_POLY, 32.0, 1), capi.FaOptions(capi.FA_EXP_POLY, 8.0, 0)):
         *_, o, lse = H.gpu_forward(x, opt)
-        H.check_forward(o, lse, o_ref, lse_ref, f"ramp {'default' if opt is None else opt.rescale_tau}")
+        label = "default" if opt is None else f"exp={opt.exp_mode} tau={opt.rescale_tau}"
+        H.check_forward(o, lse, o_ref, lse_ref, f"ramp {label}")
+
+
+@pytest.mark.parametrize("exp_mode", [0, 1], ids=["hw", "poly"])
+def test_late_score_far_above_first_max(exp_mode):
+    """One key of the last tile scores about 450 (650 in log2 units above the first tile's max):
+    the polynomial exponential must overflow to +inf there (not wrap to a tiny value), so
+    that the row takes the exact re-run in both exponential modes."""
+    B, N, NH, d = 1, 300, 2, 128
+    x = I.make_inputs(B, N, NH, NH, d, False, seed=19)
+    qf = I.bf16_bits_to_f32(x.q).reshape(B, N, NH, d) + 1.0     # every query leans towards (1, ..., 1)
+    kf = I.bf16_bits_to_f32(x.k).reshape(B, N, NH, d)
+    kf[:, 290] = 40.0                                           # key 290 scores about 450 for every query
+    x.q = I.f32_to_bf16_bits(qf)
+    x.k = I.f32_to_bf16_bits(kf)
+    o_ref, lse_ref = H.oracle_forward(x)
+    assert float(np.max(lse_ref)) > 150.0
+    *_, o, lse = H.gpu_forward(x, capi.FaOptions(exp_mode, 32.0, 1))
+    H.check_forward(o, lse, o_ref, lse_ref, f"late score exp={exp_mode}")
 
 
 def test_large_scores_stay_finite():
@@ -145,12 +170,41 @@ def test_empty_problems_are_noops():
     assert capi.fa_fwd(z, z, z, z, z, 3, 2, 2, 0, 128, 1, 0.1) == capi.FA_OK
 
 
-def test_nan_input_propagates():
+@pytest.mark.parametrize("exp_mode", [0, 1], ids=["hw", "poly"])
+def test_nan_input_propagates(exp_mode):
     x = I.make_inputs(1, 64, 1, 1, 64, False, seed=2)
     qf = I.bf16_bits_to_f32(x.q)
     qf[0, 5, 0, 3] = np.nan
     x.q = I.f32_to_bf16_bits(qf)
-    *_, o, lse = H.gpu_forward(x)
+    *_, o, lse = H.gpu_forward(x, capi.FaOptions(exp_mode, 32.0, 1))
     o = H.host_f64(o)
     assert np.all(np.isnan(o[0, 5, 0])), "a NaN query must give a NaN output row"
     assert np.all(np.isfinite(np.delete(o[0, :, 0], 5, axis=0))), "other rows stay finite"
+
+
+def test_ops_reject_mismatched_tensors():
+    """The tensor-level helpers check every tensor's shape before a pointer reaches the C ABI."""
+    q = torch.zeros((1, 64, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+    v_bad = torch.zeros((1, 32, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError):
+        ops.forward(q, k, v_bad, False)
+    with pytest.raises(ValueError):
+        ops.forward(q, k, k, False, lse=torch.zeros((1, 4, 63), dtype=torch.float32, device="cuda:0"))
+    with pytest.raises(ValueError):
+        ops.forward(q, k, k, False, out=torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16, device="cuda:0"))
+    o, lse = ops.forward(q, k, k, False)
+    with pytest.raises(ValueError):
+        ops.backward(q, k, k, o[:, :32].contiguous(), lse, o, False)
+    with pytest.raises(ValueError):
+        ops.backward(q, k, k, o, lse[:, :2].contiguous(), o, False)
+    cu = torch.tensor([0, 30, 64], dtype=torch.int32, device="cuda:0")
+    with pytest.raises(ValueError):   # packed K with another token count than Q
+        ops.forward(q[0], k[0, :60], k[0, :60], True, cu_seqlens=cu, max_seqlen=34)
+
+
+def test_negative_scale_is_rejected():
+    x = I.make_inputs(1, 64, 2, 2, 128, False, seed=4)
+    q, k, v = H.dev(x.q), H.dev(x.k), H.dev(x.v)
+    with pytest.raises(capi.FaError):
+        ops.forward(q, k, v, False, -0.1)

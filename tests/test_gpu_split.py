@@ -113,3 +113,28 @@ def test_split_workload_sampled():
             o_r, l_r = oracle.head_forward_keys(qrow, kf[:, g], vf[:, g], x.scale, True, q_off, 0, x.Nk)
             assert abs(lg[0, h, r] - l_r[0]) <= H.LSE_MAX_ABS, ("merged LSE", h, r)
             assert np.max(np.abs(og[0, r, h] - o_r[0])) <= H.O_MAX_ABS, ("merged O", h, r)
+
+
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_split_forced_rescale(tau):
+    """Scores rising along the key axis and a late spike inside every chunk: tau 0 and 8 send the
+    split kernel's workgroups through the tracking and exact passes; parts and merge match the oracle."""
+    B, Nq, Nk, Hq, Hkv, d, n = 1, 200, 900, 4, 2, 128, 3
+    x = I.make_split_inputs(B, Nq, Nk, Hq, Hkv, d, True, seed=350, n_splits=n)
+    qf = I.bf16_bits_to_f32(x.q)
+    kf = I.bf16_bits_to_f32(x.k)
+    G = Hq // Hkv
+    lean = np.sign(qf.mean(axis=1).reshape(B, Hkv, G, d).mean(axis=2))          # [B, Hkv, d]
+    kf = kf + np.linspace(0, 6, Nk, dtype=np.float32)[None, :, None, None] * lean[:, None]
+    for j in (250, 550, 880):
+        kf[:, j] += 30.0 * lean
+    x.k = I.f32_to_bf16_bits(kf)
+    q, k, v = H.dev(x.q), H.dev(x.k), H.dev(x.v)
+    opt = capi.FaOptions(capi.FA_EXP_HW, tau, 1)
+    o_part, lse_part = ops.forward_split(q, k, v, True, n, x.scale, options=opt)
+    o, lse = ops.merge(o_part, lse_part)
+    torch.cuda.synchronize()
+    op_ref, lp_ref = oracle.attention_forward_split(H.f64(x.q), H.f64(x.k), H.f64(x.v), x.scale, True, n)
+    _check_parts(o_part, lse_part, op_ref, lp_ref, f"split forced rescale tau={tau}")
+    o_ref, lse_ref = oracle.merge_partials(op_ref, lp_ref)
+    H.check_forward(o, lse, o_ref, lse_ref, f"split forced rescale tau={tau} merged")

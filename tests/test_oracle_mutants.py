@@ -140,3 +140,21 @@ def test_fp8_mutant_is_caught(name):
     exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
     with pytest.raises(AssertionError):
         pins.pin_fp8(mod.attention_forward_fp8, mod.e4m3_to_float)
+
+
+ROWDOT_MUTANTS = {
+    "rowdot_do_twice": ("d = np.sum(do * o, axis=-1)", "d = np.sum(do * do, axis=-1)"),
+    "rowdot_sums_wrong_axis": ("d = np.sum(do * o, axis=-1)", "d = np.sum(do * o, axis=-2)"),
+    "rowdot_packed_untransposed": ("    return d.T.copy()", "    return d.copy()"),
+    "rowdot_uniform_swapped_axes": ("np.transpose(d, (0, 2, 1))", "np.transpose(d, (2, 1, 0))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROWDOT_MUTANTS))
+def test_rowdot_mutant_is_caught(name):
+    old, new = ROWDOT_MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    with pytest.raises(Exception):
+        pins.pin_rowdot(mod.backward_rowdot)

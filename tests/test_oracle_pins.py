@@ -38,15 +38,8 @@ def test_row_subset_is_exact():
     assert np.all(np.isnan(o2[:, others])) and np.all(np.isnan(lse2[:, :, others]))
 
 
-def test_backward_rowdot_layout():
-    rng = np.random.default_rng(4)
-    do, o = rng.standard_normal((2, 5, 3, 4)), rng.standard_normal((2, 5, 3, 4))
-    d = oracle.backward_rowdot(do, o)
-    assert d.shape == (2, 3, 5)
-    assert np.isclose(d[1, 2, 4], float(np.dot(do[1, 4, 2], o[1, 4, 2])))
-    dp, op = rng.standard_normal((7, 3, 4)), rng.standard_normal((7, 3, 4))
-    d = oracle.backward_rowdot(dp, op)
-    assert d.shape == (3, 7) and np.isclose(d[2, 6], float(np.dot(dp[6, 2], op[6, 2])))
+def test_backward_rowdot_against_softmax_identity():
+    pins.pin_rowdot(oracle.backward_rowdot)
 
 
 def test_empty_sequence_is_skipped():
