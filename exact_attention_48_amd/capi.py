@@ -29,7 +29,8 @@ FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_fp8_ex",
-            "fa_fwd_split", "fa_fwd_split_ex", "fa_merge", "fa_exp2_eval", "fa_status_string", "fa_version")
+            "fa_fwd_split", "fa_fwd_split_ex", "fa_merge", "fa_exp2_eval", "fa_status_string", "fa_version",
+            "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace")
 
 
 class FaOptions(ctypes.Structure):
@@ -66,6 +67,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = ci
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp, sz, ci, vp]
     lib.fa_bwd_ex.restype = ci
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp]
+    lib.fa_bwd_noalloc.restype = ci
+    lib.fa_bwd_noalloc_max_workspace.argtypes = []
+    lib.fa_bwd_noalloc_max_workspace.restype = sz
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, vp]
     lib.fa_fwd_fp8.restype = ci
     lib.fa_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp,
@@ -156,6 +161,20 @@ def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B: int, Hq: int, Hkv: int, N: i
     if check and st != FA_OK:
         raise FaError(st, "fa_bwd_ex")
     return st
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B: int, Hq: int, Hkv: int, N: int, d: int, causal: int,
+                   softmax_scale: float, cu_seqlens=None, stream=None, check: bool = True) -> int:
+    st = load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), B, Hq, Hkv, N, d, int(causal), float(softmax_scale), _ptr(cu_seqlens),
+                               _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
+    return st
+
+
+def fa_bwd_noalloc_max_workspace() -> int:
+    return int(load().fa_bwd_noalloc_max_workspace())
 
 
 def fa_fwd_split(q, k, v, o_part, lse_part, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, causal: int,

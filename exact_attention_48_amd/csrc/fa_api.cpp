@@ -1,7 +1,9 @@
 // fa_api.cpp -- the C ABI (include/fa.h): validate, pick the kernel variant, launch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_exp2.h"
@@ -42,6 +44,37 @@ int xcd_chunks(int Hkv) {
   while (Hkv % g) g >>= 1;                             // gcd(Hkv, 8)
   return 8 / g;
 }
+
+// The backward's workspace for callers that cannot allocate (fa_bwd_noalloc):
+// a fixed device array, one copy per GPU, held until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch array, or nullptr on error.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
 
 }  // namespace fa
 
@@ -234,6 +267,25 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens,
                    workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+size_t fa_bwd_noalloc_max_workspace(void) { return fa::kScratchBytes; }
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                         const int32_t* cu_seqlens, void* stream) {
+  const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
+  // every argument is checked before any HIP call (the workspace is ours: needed = 0 skips its check)
+  fa_status st = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, pr, softmax_scale, cu_seqlens, nullptr, 0, 0);
+  if (st != FA_OK) return st;
+  if (fa::empty_problem(pr)) return FA_OK;
+  const size_t needed = fa::bwd_workspace_bytes(B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr);
+  if (needed > fa::kScratchBytes) return FA_ERR_WORKSPACE;
+  void* ws = fa::scratch_ptr();
+  if (!ws) return FA_ERR_HIP;
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, ws,
+                   fa::kScratchBytes, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -132,6 +132,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
                  const int32_t* cu_seqlens, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Arguments and
+ * results as for fa_bwd, without the workspace: the library keeps it in a fixed
+ * device array of fa_bwd_noalloc_max_workspace() bytes (64 MiB), one per GPU,
+ * held until the process ends. No call allocates or frees anything.
+ *   - Returns FA_ERR_WORKSPACE when fa_bwd_workspace_size(...) for these sizes
+ *     exceeds that maximum (for packed batches the bound uses B * N tokens).
+ *   - Every call on one GPU uses that GPU's single array: calls that overlap on
+ *     one GPU (on different streams, or from several host threads without
+ *     ordering) race on it and give undefined results. Calls ordered on one
+ *     stream are safe; nothing in the array needs clearing between calls.
+ *   - FA_ERR_HIP if the array's device address cannot be obtained.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                         const int32_t* cu_seqlens, void* stream);
+
+/* Size in bytes of fa_bwd_noalloc's fixed workspace array. */
+size_t fa_bwd_noalloc_max_workspace(void);
+
 /* Stages of the backward pass, for fa_bwd_ex. */
 typedef enum {
     FA_BWD_PREPROCESS = 1,  /* D_i = rowsum(dO o O) and LSE_i * log2(e) into the workspace; for

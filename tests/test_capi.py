@@ -206,3 +206,33 @@ def exp2_eval(*, x=A, y=A + 4096, n=16, mode=capi.FA_EXP_HW):
 ])
 def test_exp2_eval_rejects(lib, kw, expect):
     assert exp2_eval(**kw) == expect
+
+
+def bwd_noalloc(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0,
+                scale=0.1, cu=None)
+    args.update(kw)
+    return capi.fa_bwd_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"], args["dq"],
+                               args["dk"], args["dv"], args["B"], args["Hq"], args["Hkv"], args["N"], args["d"],
+                               args["causal"], args["scale"], args["cu"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dq=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(dk=A + 4), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=32), capi.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=4, Hkv=3), capi.FA_ERR_INVALID_ARGUMENT),
+    # 2 x 4 x 65536 x 64 x 4 bytes of D and LSE*log2(e) = 128 MiB > the fixed 64 MiB array
+    (dict(B=4, N=65536, Hq=64, Hkv=64), capi.FA_ERR_WORKSPACE),
+    (dict(B=0), capi.FA_OK),
+])
+def test_bwd_noalloc_rejects_before_launch(lib, kw, expect):
+    assert bwd_noalloc(**kw) == expect
+
+
+def test_bwd_noalloc_limit(lib):
+    assert capi.fa_bwd_noalloc_max_workspace() == 64 << 20
+    # the largest workloads here fit: the causal 8192-token backward and the packed GQA one (B * N bound)
+    assert capi.fa_bwd_workspace_size(2, 16, 16, 8192, 128, 1, 0) <= 64 << 20
+    assert capi.fa_bwd_workspace_size(16, 32, 8, 16007, 128, 1, 1) <= 64 << 20
