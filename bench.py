@@ -38,7 +38,9 @@ MAIN = "fwd_b4_h16_n4096_d128"
 # Algorithmic work of each kernel per unmasked score element, in units of d FLOP:
 # forward: S = QK^T and O = PV (4d); dK/dV kernel: S, dP, dV, dK (8d); dQ kernel:
 # the dQ product only (2d; its S and dP recomputations are not algorithmic).
-KERNEL_FLOP_PER_ELEM = {"fa_fwd_kernel": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2, "bwd_prep_kernel": 0}
+# (d = 128 forwards run fa_fwd_pp_kernel, the two-waves-per-SIMD kernel; other d run fa_fwd_kernel)
+KERNEL_FLOP_PER_ELEM = {"fa_fwd_pp_kernel": 4, "fa_fwd_kernel": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2,
+                        "bwd_prep_kernel": 0}
 
 
 def parse():
@@ -61,6 +63,7 @@ def source_hash(names):
 
 
 KERNEL_SOURCES = {
+    "fa_fwd_pp_kernel": ["fa_fwd_pp.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
     "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
     "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
     "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
@@ -151,7 +154,7 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
-    names = ["fa_fwd_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    names = ["fa_fwd_pp_kernel" if d == 128 else "fa_fwd_kernel", "bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
     kms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all(), "non-finite outputs"
 

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libfa.so")
 ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip", "fa_exp2.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_bwd.hip", "fa_merge.hip", "fa_exp2.hip"]
 
 
 def hipcc() -> str:

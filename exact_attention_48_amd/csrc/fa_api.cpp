@@ -15,6 +15,16 @@ namespace {
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kDefaultTau = 32.0f;
 
+// The exponent scale c = softmax_scale * log2(e) of the forward kernels. A zero
+// scale (uniform attention over the visible keys) becomes the smallest normal
+// float: masked scores are -inf, and -inf * 0 would give NaN where -inf * c
+// gives the -inf that exp2 turns into 0; every finite score times c is then
+// below 2^-24 in magnitude for |S| < 2^102, so exp2 of it rounds to 1.
+inline float fwd_scale_log2(float softmax_scale) {
+  const float c = softmax_scale * kLog2eF;
+  return c > 0.f ? c : 1.17549435e-38f;
+}
+
 inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -114,7 +124,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
   p.N = N;
   p.lpt = options ? options->lpt_order : 1;
   p.kv_chunks = fa::xcd_chunks(Hkv);
-  p.scale_log2 = softmax_scale * kLog2eF;
+  p.scale_log2 = fwd_scale_log2(softmax_scale);
   p.tau = options ? options->rescale_tau : kDefaultTau;
   const int expmode = options ? options->exp_mode : FA_EXP_HW;
   hipError_t e = fa::fwd_launch(p, d, causal, cu_seqlens != nullptr, expmode, (hipStream_t)stream);
@@ -149,7 +159,7 @@ fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float
   p.N = N;
   p.lpt = options ? options->lpt_order : 1;
   p.kv_chunks = fa::xcd_chunks(Hkv);
-  p.scale_log2 = softmax_scale * kLog2eF;
+  p.scale_log2 = fwd_scale_log2(softmax_scale);
   p.tau = options ? options->rescale_tau : kDefaultTau;
   p.q_descale = q_descale;
   p.k_descale = k_descale;
@@ -182,7 +192,7 @@ fa_status fa_fwd_split_ex(const void* q, const void* k, const void* v, float* o_
   p.N = Nq;
   p.lpt = options ? options->lpt_order : 1;
   p.kv_chunks = fa::xcd_chunks(Hkv);
-  p.scale_log2 = softmax_scale * kLog2eF;
+  p.scale_log2 = fwd_scale_log2(softmax_scale);
   p.tau = options ? options->rescale_tau : kDefaultTau;
   p.o_part = o_part;
   p.lse_part = lse_part;

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +57,17 @@ __device__ __forceinline__ void mfma_v_init(f32x16& acc, const bf16x8& a, const 
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// Every operand in VGPRs (kernels at two waves per SIMD, whose 256 registers
+// per wave go to the VGPRs alone; the MFMA rate is the same as with AGPR
+// accumulators):
+//   acc = A * B (accumulator start 0)
+__device__ __forceinline__ void mfma_vv_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+//   acc += A * B
+__device__ __forceinline__ void mfma_vv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
 // 8-bit MFMA: S^T (VGPR accumulator) from K (A, VGPRs) and Q^T (B, AGPRs), both
 // OCP E4M3 (format fields 0), 32 bytes of the contraction per lane and operand.
 __device__ __forceinline__ void mfma8_v_first(f32x16& acc, const i32x8& a, const i32x8& b) {
@@ -67,6 +80,24 @@ __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n s_n
 // Keeps an asm MFMA result allocated up to this point (a result that is never
 // read would otherwise free its registers while the MFMA still writes them).
 __device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
+
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// -inf where the element offset E (a compile-time constant in [0, 64]) is at
+// least thr, else x: one compare into VCC and one select, so that masking a tile
+// does not build up one SGPR pair per element.
+template <int E>
+__device__ __forceinline__ float mask_ge(float x, int thr, float ninf) {
+  asm("v_cmp_le_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc" : "+v"(x) : "v"(thr), "n"(E), "v"(ninf) : "vcc");
+  return x;
+}
 
 // Both lanes of the pair (l, l ^ 32) receive max(x[l], x[l ^ 32]).
 // Maxima as plain v_max / v_max3. fmaxf on values produced by inline asm

@@ -571,6 +571,7 @@ static hipError_t launch_fwd_d(const FwdParams& p, int grid, int causal, int var
 }
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream) {
+  if (d == 128) return fwd_pp_launch(p, causal, varlen, expmode, stream);   // two waves per SIMD (fa_fwd_pp.hip)
   p.n_qtiles = (p.N + BM - 1) / BM;
   const long grid_l = varlen ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles)
                              : q_grid_level(p.B, p.Hq, p.G, p.n_qtiles);

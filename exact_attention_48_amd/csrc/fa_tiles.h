@@ -21,15 +21,15 @@ using ic = std::integral_constant<int, N>;
 
 // HBM -> LDS copy of a ROWS x D bf16 tile of a [tokens][stride] tensor into a
 // swizzled LDS tile; rows past the sequence end are clamped to its last row.
-// All NWAVES waves take part, PER_WAVE 1 KiB instructions each.
-template <int D, int ROWS>
+// All NW waves of the workgroup take part, PER_WAVE 1 KiB instructions each.
+template <int D, int ROWS, int NW = NWAVES>
 struct RowCopy {
   static constexpr int ROWB = D * 2;
   static constexpr int LPR = ROWB / 16;          // lanes per row
   static constexpr int RPI = 64 / LPR;           // rows per instruction
   static constexpr int NI = ROWS / RPI;          // instructions per tile
-  static constexpr int PER_WAVE = NI / NWAVES;
-  static_assert(PER_WAVE * NWAVES == NI, "tile copy must split evenly over the waves");
+  static constexpr int PER_WAVE = NI / NW;
+  static_assert(PER_WAVE * NW == NI, "tile copy must split evenly over the waves");
   unsigned off[PER_WAVE];                        // row * stride + swizzled chunk * 16
   int wave, lane;
 

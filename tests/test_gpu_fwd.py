@@ -208,3 +208,16 @@ def test_negative_scale_is_rejected():
     q, k, v = H.dev(x.q), H.dev(x.k), H.dev(x.v)
     with pytest.raises(capi.FaError):
         ops.forward(q, k, v, False, -0.1)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_uniform_weights(d, causal):
+    """Scale 0: every visible key gets the same weight, masked keys none (O = mean of the visible
+    V rows, LSE = ln of their count); no NaN from a masked score times a zero scale."""
+    x = I.make_inputs(1, 300, 2, 2, d, causal, seed=6, scale=0.0)
+    o_ref, lse_ref = H.oracle_forward(x)
+    *_, o, lse = H.gpu_forward(x)
+    H.check_forward(o, lse, o_ref, lse_ref, f"scale 0 d={d} causal={causal}")
+    n_vis = np.arange(1, 301) if causal else np.full(300, 300)
+    np.testing.assert_allclose(H.host_f64(lse)[0, 0], np.log(n_vis), atol=1e-3)
