@@ -17,7 +17,6 @@ on this machine's host cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -26,6 +25,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+from exact_attention_48_amd.kernel_sources import source_hash  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz (AMD: "2.5 PFLOP/s" dense BF16)
 PEAK_FP8_TFLOPS = 5033.2      # dense 8-bit MFMA, twice the bf16 rate (AMD: "5.0 PFLOP/s")
@@ -39,8 +40,22 @@ MAIN = "fwd_b4_h16_n4096_d128"
 # forward: S = QK^T and O = PV (4d); dK/dV kernel: S, dP, dV, dK (8d); dQ kernel:
 # the dQ product only (2d; its S and dP recomputations are not algorithmic).
 # (d = 128 forwards run fa_fwd_pp_kernel, the two-waves-per-SIMD kernel; other d run fa_fwd_kernel)
+FWD_OPTION_TIMINGS = {}
 KERNEL_FLOP_PER_ELEM = {"fa_fwd_pp_kernel": 4, "fa_fwd_kernel": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2,
                         "bwd_prep_kernel": 0}
+
+
+# Forward timings under non-default options, beside the default (v_exp_f32, tau = 32,
+# heaviest tiles first): the software exponential, the plain tile order, and tau = 0,
+# which sends every workgroup through the tracking and exact re-run passes (the cost
+# of the conditional-rescale fallback when it fires everywhere).
+def _fwd_option_timings():
+    from exact_attention_48_amd import capi
+    poly = ("exp_poly", capi.FaOptions(capi.FA_EXP_POLY, 32.0, 1))
+    lpt0 = ("lpt0", capi.FaOptions(capi.FA_EXP_HW, 32.0, 0))
+    tau0 = ("tau0_rerun", capi.FaOptions(capi.FA_EXP_HW, 0.0, 1))
+    return {"fwd_b4_h16_n4096_d128": [poly, tau0], "fwd_causal_b2_h16_n16384_d128": [poly, lpt0, tau0],
+            "fwd_causal_varlen16_hq32_hkv8_d128": [lpt0]}
 
 
 def parse():
@@ -52,23 +67,6 @@ def parse():
     ap.add_argument("--main-only", action="store_true", help="skip the per-workload figures")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = auto)")
     return ap.parse_args()
-
-
-def source_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "exact_attention_48_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-KERNEL_SOURCES = {
-    "fa_fwd_pp_kernel": ["fa_fwd_pp.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
-    "fa_fwd_kernel": ["fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
-    "bwd_dkdv_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
-    "bwd_dq_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
-    "bwd_prep_kernel": ["fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_order.h", "fa_tiles.h"],
-}
 
 
 def read_traffic(kernel, workload):
@@ -83,7 +81,7 @@ def read_traffic(kernel, workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+    if vals.get("source_hash") != source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -108,6 +106,8 @@ def main():
         sys.exit(1)
     capi.load()
     dev = torch.device("cuda:0")
+    global FWD_OPTION_TIMINGS
+    FWD_OPTION_TIMINGS = _fwd_option_timings()
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -232,11 +232,19 @@ def main():
             fwd = lambda: capi.fa_fwd(qw, kw, vw, ow, lse_w, wl.B, wl.Hq, wl.Hkv, Nw, wl.d, int(wl.causal),
                                       wl.scale, cu, stream)
             ent = {}
-            ms_f = time_it(fwd, 5 if Nw >= 8192 else 20)
+            reps_f = 5 if Nw >= 8192 else 20
+            ms_f = time_it(fwd, reps_f)
             fl = I.counted_flops(lens, wl.Hq, wl.d, wl.causal)
             ent["fwd_ms"] = round(ms_f, 4)
             ent["fwd_tflops"] = round(fl / (ms_f * 1e-3) / 1e12, 1)
             ent["fwd_frac_of_peak"] = round(fl / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            # the same forward under other options (same inputs, same launch shape)
+            for label, opt in FWD_OPTION_TIMINGS.get(name, ()):
+                fx = lambda: capi.fa_fwd_ex(qw, kw, vw, ow, lse_w, wl.B, wl.Hq, wl.Hkv, Nw, wl.d, int(wl.causal),
+                                            wl.scale, cu, opt, stream)
+                ms_x = time_it(fx, reps_f)
+                ent[f"fwd_{label}_ms"] = round(ms_x, 4)
+                ent[f"fwd_{label}_vs_default"] = round(ms_x / ms_f, 3)
             if wl.kind == "bwd":
                 dow = rnd(qs, wl.seed * 10 + 4)
                 dqw, dkw, dvw = torch.empty_like(qw), torch.empty_like(kw), torch.empty_like(vw)

@@ -12,6 +12,8 @@ Meant to run under ``rocprofv3 --pmc ...`` (or ``--kernel-trace``):
               scaled N(0,1) draw, descale 1/64)
 --part copy   a plain device-to-device copy of 512 MiB (known byte count, used
               to calibrate FETCH_SIZE / WRITE_SIZE against real HBM bytes)
+--exp-mode, --tau, --lpt   forward options (fa_fwd_ex) for --part fwd / bwd
+Summaries of the profiler's CSV output: ``python -m exact_attention_48_amd.profile_summary``.
 Inputs are seeded N(0,1) bf16 drawn on the GPU with the workload's shapes.
 """
 from __future__ import annotations
@@ -30,6 +32,9 @@ def main():
     ap.add_argument("--workload", default="fwd_b4_h16_n4096_d128", choices=sorted(I.WORKLOADS))
     ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "split", "fp8", "copy"])
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--exp-mode", type=int, default=capi.FA_EXP_HW, choices=[capi.FA_EXP_HW, capi.FA_EXP_POLY])
+    ap.add_argument("--tau", type=float, default=32.0)
+    ap.add_argument("--lpt", type=int, default=1, choices=[0, 1])
     args = ap.parse_args()
     dev = torch.device("cuda:0")
     if args.part == "copy":
@@ -88,7 +93,8 @@ def main():
     q, k, v = rnd(qs), rnd(ks), rnd(ks)
     o = torch.empty_like(q)
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
-    fwd = lambda: capi.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), w.scale, cu)
+    opt = capi.FaOptions(args.exp_mode, args.tau, args.lpt)
+    fwd = lambda: capi.fa_fwd_ex(q, k, v, o, lse, w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), w.scale, cu, opt)
     if args.part == "fwd":
         for _ in range(args.reps):
             fwd()
