@@ -318,13 +318,32 @@ def e4m3_to_float(bits: np.ndarray) -> np.ndarray:
     return np.where((b & 0x7F) == 0x7F, np.nan, out)
 
 
+# Tokens per descale block of the block-scaled 8-bit inputs: block j of a
+# sequence holds its tokens 64 j .. 64 j + 63 (positions local to the sequence).
+FP8_SCALE_BLOCK = 64
+
+
+def _token_descales(desc: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Descale of every token of one sequence, [n_tokens, H], from one sequence's
+    descales: [H] (one per head) or [H, nb] (one per head and 64-token block)."""
+    desc = np.asarray(desc, dtype=np.float64)
+    if desc.ndim == 1:
+        return np.broadcast_to(desc[None, :], (n_tokens, desc.shape[0]))
+    block = np.arange(n_tokens) // FP8_SCALE_BLOCK
+    return desc[:, block].T
+
+
 def attention_forward_fp8(q8: np.ndarray, k8: np.ndarray, v: np.ndarray, q_descale: np.ndarray,
                           k_descale: np.ndarray, scale: float, causal: bool,
                           cu_seqlens: Optional[np.ndarray] = None, rows: RowSelect = None):
     """Exact attention of the dequantised FP8 inputs. Returns (O, LSE) in float64.
 
-    q8, k8: uint8 E4M3 in the Q / K layouts; v: float64 values in the V layout;
-    q_descale [B, Hq], k_descale [B, Hkv] (B = number of sequences when packed).
+    q8, k8: uint8 E4M3 in the Q / K layouts; v: float64 values in the V layout.
+    Descales, B = number of sequences when packed: per (sequence, head),
+    q_descale [B, Hq] and k_descale [B, Hkv]; or per 64-token block of each
+    (sequence, head), q_descale [B, Hq, nb] and k_descale [B, Hkv, nb], where
+    token t of a sequence (local position) uses block t // 64. An element's
+    value is its code times its descale.
     """
     packed = cu_seqlens is not None
     q = e4m3_to_float(q8)
@@ -334,9 +353,11 @@ def attention_forward_fp8(q8: np.ndarray, k8: np.ndarray, v: np.ndarray, q_desca
     if packed:
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         for s in range(len(cu) - 1):
-            q[cu[s]:cu[s + 1]] *= qd[s][None, :, None]
-            k[cu[s]:cu[s + 1]] *= kd[s][None, :, None]
+            L = int(cu[s + 1] - cu[s])
+            q[cu[s]:cu[s + 1]] *= _token_descales(qd[s], L)[:, :, None]
+            k[cu[s]:cu[s + 1]] *= _token_descales(kd[s], L)[:, :, None]
     else:
-        q *= qd[:, None, :, None]
-        k *= kd[:, None, :, None]
+        for b in range(q.shape[0]):
+            q[b] *= _token_descales(qd[b], q.shape[1])[:, :, None]
+            k[b] *= _token_descales(kd[b], k.shape[1])[:, :, None]
     return attention_forward(q, k, v, scale, causal, cu_seqlens, rows)

@@ -492,6 +492,56 @@ def pin_fp8(fwd8, decode):
         assert np.max(np.abs(lse - np.array(lb))) < TOL, ("FP8 LSE vs brute force", B, N, causal, lens)
 
 
+def pin_fp8_blocks(fwd8):
+    """Block-scaled 8-bit inputs: one descale per 64-token block of each (sequence, head),
+    block t // 64 for the token at local position t. The forward equals brute force (pure
+    Python) on inputs dequantised code by code, each element with the scale its sequence,
+    head and local position select, uniform and packed (sequences of 1 to 3 blocks, one
+    ending mid-block); and block descales that are all equal give exactly the result of
+    the per-(sequence, head) descales."""
+    rng = np.random.default_rng(37)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for (B, N, Hq, Hkv, d, causal, lens) in [(1, 150, 2, 1, 3, True, None), (2, 70, 2, 2, 2, False, None),
+                                             (0, 0, 2, 2, 2, False, [70, 130, 5])]:
+        if lens is None:
+            qs, ks, nseq, nmax = (B, N, Hq, d), (B, N, Hkv, d), B, N
+            cu = None
+        else:
+            T = sum(lens)
+            qs, ks, nseq, nmax = (T, Hq, d), (T, Hkv, d), len(lens), max(lens)
+            cu = _cu(lens)
+        nb = (nmax + 63) // 64
+        q8 = rng.choice(finite, size=qs)
+        k8 = rng.choice(finite, size=ks)
+        v = _rand(rng, *ks)
+        qd = rng.uniform(0.002, 0.02, size=(nseq, Hq, nb))
+        kd = rng.uniform(0.002, 0.02, size=(nseq, Hkv, nb))
+        scale = 0.3
+        o, lse = fwd8(q8, k8, v, qd, kd, scale, causal, cu)
+
+        def deq(codes, desc, shape):
+            out = np.zeros(shape)
+            for idx in np.ndindex(*shape):
+                if cu is None:
+                    s, pos = idx[0], idx[1]
+                else:
+                    s = int(np.searchsorted(cu, idx[0], side="right") - 1)
+                    pos = idx[0] - int(cu[s])
+                out[idx] = _e4m3_py(int(codes[idx])) * desc[s, idx[-2], pos // 64]
+            return out
+        qf, kf = deq(q8, qd, qs), deq(k8, kd, ks)
+        if cu is None:
+            ob, lb = bruteforce.forward(qf.tolist(), kf.tolist(), v.tolist(), scale, causal)
+        else:
+            ob, lb = bruteforce.forward(qf.tolist(), kf.tolist(), v.tolist(), scale, causal, cu.tolist())
+        assert np.max(np.abs(o - np.array(ob))) < TOL, ("FP8 block O vs brute force", B, N, causal, lens)
+        assert np.max(np.abs(lse - np.array(lb))) < TOL, ("FP8 block LSE vs brute force", B, N, causal, lens)
+        # equal blocks reduce to per-(sequence, head) descales
+        o1, l1 = fwd8(q8, k8, v, qd[:, :, :1].repeat(nb, axis=2), kd[:, :, :1].repeat(nb, axis=2), scale, causal, cu)
+        o2, l2 = fwd8(q8, k8, v, qd[:, :, 0], kd[:, :, 0], scale, causal, cu)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "equal block descales != per-head descales"
+
+
 def pin_rowdot(rowdot):
     """D_i = dO_i . O_i equals sum_j P_ij dP_ij with dP_ij = dO_i . V_j (O_i = sum_j P_ij V_j):
     P and O from the pure-Python brute force, the double sum in math.fsum, for uniform and

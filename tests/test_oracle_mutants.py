@@ -126,10 +126,35 @@ FP8_MUTANTS = {
     "mantissa_over_16": ("(1.0 + m / 8.0) * np.exp2", "(1.0 + m / 16.0) * np.exp2"),
     "nan_code_missed": ("return np.where((b & 0x7F) == 0x7F, np.nan, out)", "return out"),
     "sign_dropped": ("sign = np.where(b & 0x80, -1.0, 1.0)", "sign = np.where(b & 0x80, 1.0, 1.0)"),
-    "q_descale_sequence_order": ("q *= qd[:, None, :, None]", "q *= qd[::-1][:, None, :, None]"),
-    "k_scaled_by_q_descale": ("k *= kd[:, None, :, None]", "k *= qd[:, None, :kd.shape[1], None]"),
-    "packed_descale_first_sequence": ("q[cu[s]:cu[s + 1]] *= qd[s][None, :, None]", "q[cu[s]:cu[s + 1]] *= qd[0][None, :, None]"),
+    "q_descale_sequence_order": ("q[b] *= _token_descales(qd[b], q.shape[1])", "q[b] *= _token_descales(qd[-1 - b], q.shape[1])"),
+    "k_scaled_by_q_descale": ("k[b] *= _token_descales(kd[b], k.shape[1])", "k[b] *= _token_descales(qd[b][:kd.shape[1]], k.shape[1])"),
+    "packed_descale_first_sequence": ("q[cu[s]:cu[s + 1]] *= _token_descales(qd[s], L)", "q[cu[s]:cu[s + 1]] *= _token_descales(qd[0], L)"),
 }
+
+# Mistakes in the block-scaled dequantisation, each caught by pin_fp8_blocks.
+FP8_BLOCK_MUTANTS = {
+    "block_of_32_tokens": ("    block = np.arange(n_tokens) // FP8_SCALE_BLOCK",
+                           "    block = np.minimum(np.arange(n_tokens) // 32, desc.shape[1] - 1)"),
+    "block_off_by_one": ("    block = np.arange(n_tokens) // FP8_SCALE_BLOCK",
+                         "    block = np.minimum((np.arange(n_tokens) + 1) // FP8_SCALE_BLOCK, desc.shape[1] - 1)"),
+    "first_block_everywhere": ("    return desc[:, block].T", "    return desc[:, 0 * block].T"),
+    "blocks_transposed": ("    return desc[:, block].T", "    return desc[:, block].T[::-1]"),
+    "packed_block_from_global_position": (
+        "            q[cu[s]:cu[s + 1]] *= _token_descales(qd[s], L)[:, :, None]",
+        "            q[cu[s]:cu[s + 1]] *= _token_descales(qd[s], int(cu[s + 1]))[int(cu[s]):, :, None]"),
+    "k_head_0_descales_for_every_head": ("            k[b] *= _token_descales(kd[b], k.shape[1])[:, :, None]",
+                                       "            k[b] *= _token_descales(kd[b][:1].repeat(kd.shape[1], axis=0), k.shape[1])[:, :, None]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_BLOCK_MUTANTS))
+def test_fp8_block_mutant_is_caught(name):
+    old, new = FP8_BLOCK_MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    with pytest.raises(Exception):   # a wrong value (AssertionError) or a block index past the array
+        pins.pin_fp8_blocks(mod.attention_forward_fp8)
 
 
 @pytest.mark.parametrize("name", sorted(FP8_MUTANTS))

@@ -64,3 +64,7 @@ def test_split_and_merge_pins():
 
 def test_fp8_pins():
     pins.pin_fp8(oracle.attention_forward_fp8, oracle.e4m3_to_float)
+
+
+def test_pin_fp8_blocks():
+    pins.pin_fp8_blocks(oracle.attention_forward_fp8)
