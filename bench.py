@@ -278,10 +278,19 @@ def main():
                                          int(wl.causal), wl.scale, None, stream)
             ms = time_it(f8, 5 if wl.N >= 8192 else 20)
             fl = I.counted_flops(np.full(wl.B, wl.N), wl.Hq, wl.d, wl.causal)
+            # the same codes with one descale per 64-token block (all 1/64)
+            nb = (wl.N + 63) // 64
+            qdb = torch.full((wl.B, wl.Hq, nb), 1.0 / 64, dtype=torch.float32, device=dev)
+            kdb = torch.full((wl.B, wl.Hkv, nb), 1.0 / 64, dtype=torch.float32, device=dev)
+            f8b = lambda: capi.fa_fwd_fp8_blockscale(q8, k8, vw, qdb, kdb, ow, lw, wl.B, wl.Hq, wl.Hkv, wl.N, wl.d,
+                                                     int(wl.causal), wl.scale, None, None, stream)
+            ms_b = time_it(f8b, 5 if wl.N >= 8192 else 20)
             workloads[name] = {"fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                                "fwd_frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                               "fwd_frac_of_qk8_pv16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_QK8_PV16_TFLOPS, 4)}
-            del q8, k8, vw, qd, kd, ow, lw
+                               "fwd_frac_of_qk8_pv16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_QK8_PV16_TFLOPS, 4),
+                               "fwd_blockscale_ms": round(ms_b, 4),
+                               "fwd_blockscale_tflops": round(fl / (ms_b * 1e-3) / 1e12, 1)}
+            del q8, k8, vw, qd, kd, ow, lw, qdb, kdb
             torch.cuda.empty_cache()
 
         # split-KV partial results + merge: 512 queries against 131072 keys

@@ -29,6 +29,7 @@ FA_BWD_DQ = 4
 FA_BWD_ALL = 7
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_fp8_ex",
+            "fa_fwd_fp8_blockscale",
             "fa_fwd_split", "fa_fwd_split_ex", "fa_merge", "fa_exp2_eval", "fa_status_string", "fa_version",
             "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace")
 
@@ -76,6 +77,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp,
                                   ctypes.POINTER(FaOptions), vp]
     lib.fa_fwd_fp8_ex.restype = ci
+    lib.fa_fwd_fp8_blockscale.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp,
+                                          ctypes.POINTER(FaOptions), vp]
+    lib.fa_fwd_fp8_blockscale.restype = ci
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.fa_fwd_split.restype = ci
     lib.fa_fwd_split_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, ctypes.POINTER(FaOptions), vp]
@@ -231,4 +235,16 @@ def fa_fwd_fp8_ex(q8, k8, v, q_descale, k_descale, o, lse, B: int, Hq: int, Hkv:
                               _stream(stream))
     if check and st != FA_OK:
         raise FaError(st, "fa_fwd_fp8_ex")
+    return st
+
+
+def fa_fwd_fp8_blockscale(q8, k8, v, q_descale, k_descale, o, lse, B: int, Hq: int, Hkv: int, N: int, d: int,
+                          causal: int, softmax_scale: float, cu_seqlens=None, options: Optional[FaOptions] = None,
+                          stream=None, check: bool = True) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    st = load().fa_fwd_fp8_blockscale(_ptr(q8), _ptr(k8), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(o),
+                                      _ptr(lse), B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+                                      _ptr(cu_seqlens), opt, _stream(stream))
+    if check and st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8_blockscale")
     return st

@@ -137,13 +137,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens, nullptr, stream);
 }
 
-fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float* q_descale,
-                        const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
-                        int causal, float softmax_scale, const int32_t* cu_seqlens,
-                        const fa_fwd_options* options, void* stream) {
+namespace {
+
+fa_status fwd_fp8_common(const void* q, const void* k, const void* v, const float* q_descale,
+                         const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                         int causal, float softmax_scale, const int32_t* cu_seqlens,
+                         const fa_fwd_options* options, bool blockscale, void* stream) {
   const fa::Problem pr{B, Hq, Hkv, N, d, causal, cu_seqlens != nullptr};
   fa_status st = fa::check_fp8(q, k, v, q_descale, k_descale, o, lse, pr, softmax_scale, cu_seqlens, options);
   if (st != FA_OK) return st;
+  const long nb = ((long)N + fa::kFp8Block - 1) / fa::kFp8Block;
+  if (blockscale && nb > fa::kFp8MaxBlocks) return FA_ERR_UNSUPPORTED;
   if (fa::empty_problem(pr)) return FA_OK;
   fa::FwdParams p{};
   p.q = q;
@@ -163,8 +167,29 @@ fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float
   p.tau = options ? options->rescale_tau : kDefaultTau;
   p.q_descale = q_descale;
   p.k_descale = k_descale;
-  hipError_t e = fa::fwd_fp8_launch(p, causal, cu_seqlens != nullptr, (hipStream_t)stream);
+  p.fp8_nb = blockscale ? (int)nb : 1;
+  hipError_t e = fa::fwd_fp8_launch(p, causal, cu_seqlens != nullptr, blockscale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float softmax_scale, const int32_t* cu_seqlens,
+                        const fa_fwd_options* options, void* stream) {
+  return fwd_fp8_common(q, k, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens,
+                        options, false, stream);
+}
+
+fa_status fa_fwd_fp8_blockscale(const void* q, const void* k, const void* v, const float* q_descale,
+                                const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                                int d, int causal, float softmax_scale, const int32_t* cu_seqlens,
+                                const fa_fwd_options* options, void* stream) {
+  static_assert(FA_FP8_SCALE_BLOCK == fa::kFp8Block && FA_FP8_MAX_BLOCKS == fa::kFp8MaxBlocks,
+                "the header's block constants must match the kernel's");
+  return fwd_fp8_common(q, k, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, cu_seqlens,
+                        options, true, stream);
 }
 
 fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,

@@ -82,11 +82,15 @@ struct FwdStage {
 // as fp32 O_p and LSE_p; uniform batches only.
 // FP8: Q and K as OCP E4M3 codes with per-(sequence, head) descales; S^T by the
 // 32x32x64 8-bit MFMA (64 of the contraction per instruction), V and P bf16.
-template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT, bool FP8>
+// BLK (with FP8): one descale per 64-token block of each (sequence, head)
+// instead. The exp2 factor then differs per tile and per query block, so the
+// row maxima are kept in scaled units (S c) rather than raw scores.
+template <int D, bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT, bool FP8, bool BLK = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(const FwdParams p) {
   static_assert(!(SPLIT && VARLEN), "split-KV partial results are for uniform batches");
   static_assert(!(SPLIT && FP8) && (!FP8 || D == 128), "8-bit Q/K: plain forward, d = 128");
+  static_assert(!BLK || FP8, "block descales are for 8-bit inputs");
   using S = FwdStage<D, FP8>;
   using RCK = RowCopy<FP8 ? D / 2 : D, BN>;         // an 8-bit row of D bytes copies like a bf16 row of D / 2
   using RCV = RowCopy<D, BN>;
@@ -215,7 +219,38 @@ void fa_fwd_kernel(const FwdParams p) {
   // exp2 argument scale: softmax_scale * log2(e), times the Q and K descales of
   // this (sequence, head) for 8-bit inputs
   float c = p.scale_log2;
-  if constexpr (FP8) c = c * p.q_descale[(long)s * p.Hq + h] * p.k_descale[(long)s * p.Hkv + hkv];
+  if constexpr (FP8 && !BLK) c = c * p.q_descale[(long)s * p.Hq + h] * p.k_descale[(long)s * p.Hkv + hkv];
+  // Block descales: the K descales of this (sequence, K/V head) go to LDS once
+  // (kd_lds[j] for keys 64 j ..); each query block's Q descale folds into c_q.
+  // The exp2 factor of a tile is ct = c_q * kd (at least the smallest normal
+  // float, so that a masked -inf score never meets a zero factor).
+  __shared__ float kd_lds[BLK ? kFp8MaxBlocks : 1];
+  float c_q[2] = {c, c};
+  int kd_last = 0;                           // last K block of the sequence
+  if constexpr (BLK) {
+    const int nbk = min((Lk + kFp8Block - 1) / kFp8Block, p.fp8_nb);   // (host: fp8_nb <= kFp8MaxBlocks)
+    kd_last = nbk - 1;
+    const float* kdp = p.k_descale + ((long)s * p.Hkv + hkv) * p.fp8_nb;
+    for (int i = threadIdx.x; i < nbk; i += NTHREADS) kd_lds[i] = kdp[i];
+    const float* qdp = p.q_descale + ((long)s * p.Hq + h) * p.fp8_nb;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qr = my_q[qb] < L ? my_q[qb] : L - 1;
+      c_q[qb] = c * qdp[min(qr / kFp8Block, p.fp8_nb - 1)];
+    }
+    __syncthreads();
+  }
+  auto kd_of = [&](int k0) __attribute__((always_inline)) -> float {   // K descale of the tile at key k0
+    if constexpr (BLK) return kd_lds[min(k0 / kFp8Block, kd_last)];
+    else return 1.f;
+  };
+  auto set_factor = [&](float kd, float (&ct)[2]) __attribute__((always_inline)) {
+    if constexpr (BLK) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) ct[qb] = fmaxf(c_q[qb] * kd, 1.17549435e-38f);
+    }
+  };
+  float ctA[2] = {c, c}, ctB[2] = {c, c};    // exp2 factor of the tile whose S^T is in sA / sB
   const float tau = p.tau;
   f32x16 oacc[2][DBLK];
   float m_run[2];                            // the max O and l are relative to (fixed in a pass)
@@ -259,10 +294,10 @@ void fa_fwd_kernel(const FwdParams p) {
   // of the same slot: step t does x_t = S c - m c, p_{t-1} = exp2(x_{t-1}),
   // and l += p_{t-2} (packing the bf16 pair when t-2 is odd).
   float xq[3], pq[3];
-  auto exp_step = [&](const f32x16 (&sc)[2], int t) __attribute__((always_inline)) {
+  auto exp_step = [&](const f32x16 (&sc)[2], int t, const float (&ct)[2]) __attribute__((always_inline)) {
     if (t < 32) {
       const int qb = t >> 4, r = t & 15;
-      xq[t % 3] = __builtin_fmaf(sc[qb][r], c, -mc[qb]);
+      xq[t % 3] = __builtin_fmaf(sc[qb][r], BLK ? ct[qb] : c, -mc[qb]);
     }
     if (t >= 1 && t <= 32) pq[(t - 1) % 3] = exp2_sel<EXPMODE>(xq[(t - 1) % 3]);
     if (t >= 2 && t <= 33) {
@@ -296,10 +331,16 @@ void fa_fwd_kernel(const FwdParams p) {
     if (half == 0) mpart[qb] = vmax(m, sx[qb][r + 7]);
     else mpart[qb] = vmax3(mpart[qb], m, sx[qb][r + 7]);
   };
-  auto decide = [&](int qb) __attribute__((always_inline)) {
+  auto decide = [&](int qb, const float (&ct)[2]) __attribute__((always_inline)) {
     const float mx = pair_max(mpart[qb]);
-    m_seen[qb] = vmax(m_seen[qb], mx);
-    over[qb] = over[qb] || ((mx - m_run[qb]) * c > tau);   // false when both are -inf
+    if constexpr (BLK) {                     // scaled units: m_run and m_seen are maxima of S ct
+      const float mxs = mx * ct[qb];
+      m_seen[qb] = vmax(m_seen[qb], mxs);
+      over[qb] = over[qb] || (mxs - m_run[qb] > tau);    // false when both are -inf
+    } else {
+      m_seen[qb] = vmax(m_seen[qb], mx);
+      over[qb] = over[qb] || ((mx - m_run[qb]) * c > tau);   // false when both are -inf
+    }
   };
   // ---- one iteration's MFMA stream ----
   // The 34 exp pipeline steps of a tile are spread over three phases:
@@ -316,7 +357,9 @@ void fa_fwd_kernel(const FwdParams p) {
   static_assert(KB2 + UA >= 18 && UB >= 0, "P of query block 0 must be complete before phase B1");
   constexpr int VPRE = (PFA < NV) ? PFA : NV;       // V^T fragments read during phase A
   auto stream = [&](const char FA_LDS* nt, const char FA_LDS* ct, f32x16 (&sx)[2], const f32x16 (&sc)[2],
-                    int k_next, bool issue, char FA_LDS* issue_stage, bool track) __attribute__((always_inline)) {
+                    float (&fx)[2], const float (&fc)[2], int k_next, bool issue, char FA_LDS* issue_stage,
+                    bool track) __attribute__((always_inline)) {
+    const float kd_next = kd_of(k_next);            // read early; used in phase B2
     AFrag qa[PFA];
 #pragma unroll
     for (int i = 0; i < PFA; ++i) qa[i] = a_frag(nt, i);
@@ -334,7 +377,7 @@ void fa_fwd_kernel(const FwdParams p) {
         const int j = 2 * ks + x;
         a_step(sx, j, a);
 #pragma unroll
-        for (int t = KB2 + UA * j / NA; t < KB2 + UA * (j + 1) / NA; ++t) exp_step(sc, t);
+        for (int t = KB2 + UA * j / NA; t < KB2 + UA * (j + 1) / NA; ++t) exp_step(sc, t, fc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -345,7 +388,7 @@ void fa_fwd_kernel(const FwdParams p) {
       if (f + VPRE < NV) vf[f + VPRE] = v_frag(ct, f + VPRE);
       mfma_a(oacc[0][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[0][f / DBLK]));
 #pragma unroll
-      for (int t = KB2 + UA + UB * f / NV; t < KB2 + UA + UB * (f + 1) / NV; ++t) exp_step(sc, t);
+      for (int t = KB2 + UA + UB * f / NV; t < KB2 + UA + UB * (f + 1) / NV; ++t) exp_step(sc, t, fc);
       __builtin_amdgcn_sched_barrier(0);
     }
     // phase B2: O_1 += V^T P_1, with the next tile's masking (and, in a
@@ -358,16 +401,17 @@ void fa_fwd_kernel(const FwdParams p) {
     for (int f = 0; f < NV; ++f) {
       mfma_a(oacc[1][f % DBLK], vf[f], __builtin_bit_cast(bf16x8, pb[1][f / DBLK]));
       if (f == 0 && mask_next) mask_tile(sx, k_next);
+      if (f == 0) set_factor(kd_next, fx);
       if (f == 1 && track) {
         max_half(sx, 0, 0);
         max_half(sx, 0, 1);
         max_half(sx, 1, 0);
         max_half(sx, 1, 1);
-        decide(0);
-        decide(1);
+        decide(0, fx);
+        decide(1, fx);
       }
 #pragma unroll
-      for (int t = KB2 * f / NV; t < KB2 * (f + 1) / NV; ++t) exp_step(sx, t);
+      for (int t = KB2 * f / NV; t < KB2 * (f + 1) / NV; ++t) exp_step(sx, t, fx);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -384,8 +428,8 @@ void fa_fwd_kernel(const FwdParams p) {
     const bool issue = i + 3 < n_it;
     char FA_LDS* const nst = stage((BI + 3) % NSTAGE);
     const int k_next = kb + (i + 1) * BN;
-    if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, k_next, issue, nst, track);
-    else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, k_next, issue, nst, track);
+    if constexpr (BI % 2 == 0) stream(stage((BI + 1) % NSTAGE), stage(BI), sB, sA, ctB, ctA, k_next, issue, nst, track);
+    else stream(stage((BI + 1) % NSTAGE), stage(BI), sA, sB, ctA, ctB, k_next, issue, nst, track);
   };
 
   // Rescaling, taken out of the loop. In the first pass each row's max m is
@@ -446,19 +490,20 @@ void fa_fwd_kernel(const FwdParams p) {
     }
     mfma_result_wait();
     if (needs_mask(kb)) mask_tile(sA, kb);
+    set_factor(kd_of(kb), ctA);
     max_half(sA, 0, 0);
     max_half(sA, 0, 1);
     max_half(sA, 1, 0);
     max_half(sA, 1, 1);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mx = pair_max(mpart[qb]);
+      const float mx = BLK ? pair_max(mpart[qb]) * ctA[qb] : pair_max(mpart[qb]);
       m_seen[qb] = mx;
       if (pass < 2) m_run[qb] = mx;
-      mc[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb] * c;
+      mc[qb] = m_run[qb] == -INFINITY ? 0.f : (BLK ? m_run[qb] : m_run[qb] * c);
     }
 #pragma unroll
-    for (int t = 0; t < KB2; ++t) exp_step(sA, t);
+    for (int t = 0; t < KB2; ++t) exp_step(sA, t, ctA);
 
     for (int i = 0; i < n_it; i += NSTAGE) {
       iter(ic<0>{}, i, track);
@@ -524,7 +569,8 @@ void fa_fwd_kernel(const FwdParams p) {
     }
     store_rows_bf16<D>(st, oacc[qb], inv, obase, q_row_stride, qw0 + 32 * qb, L, lane);
     if (hl == 0 && my_q[qb] < L) {
-      const float lse = (m_run[qb] == -INFINITY) ? -INFINITY : (m_run[qb] * c + __log2f(l_tot)) * kLn2;
+      const float lse = (m_run[qb] == -INFINITY) ? -INFINITY
+                                                 : ((BLK ? m_run[qb] : m_run[qb] * c) + __log2f(l_tot)) * kLn2;
       long li;
       if constexpr (VARLEN) li = (long)h * p.cu_seqlens[p.B] + seq0 + my_q[qb];
       else li = ((long)s * p.Hq + h) * p.N + my_q[qb];
@@ -548,11 +594,16 @@ static hipError_t launch_split(const FwdParams& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool BLK>
 static hipError_t launch_fp8(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<128, CAUSAL, VARLEN, 0, false, true>), dim3(grid), dim3(NTHREADS), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa_fwd_kernel<128, CAUSAL, VARLEN, 0, false, true, BLK>), dim3(grid), dim3(NTHREADS), 0,
+                     stream, p);
   return hipGetLastError();
+}
+
+template <bool CAUSAL, bool VARLEN>
+static hipError_t launch_fp8_b(const FwdParams& p, int grid, bool blk, hipStream_t stream) {
+  return blk ? launch_fp8<CAUSAL, VARLEN, true>(p, grid, stream) : launch_fp8<CAUSAL, VARLEN, false>(p, grid, stream);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -592,15 +643,17 @@ hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream) 
   return causal ? launch_split<64, true>(p, grid, stream) : launch_split<64, false>(p, grid, stream);
 }
 
-hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, hipStream_t stream) {
+hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, bool blockscale, hipStream_t stream) {
   p.n_qtiles = (p.N + BM - 1) / BM;
   const long grid_l = varlen ? q_grid_xcd(p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles)
                              : q_grid_level(p.B, p.Hq, p.G, p.n_qtiles);
   if (grid_l == 0) return hipSuccess;
   if (grid_l > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const int grid = (int)grid_l;
-  if (causal) return varlen ? launch_fp8<true, true>(p, grid, stream) : launch_fp8<true, false>(p, grid, stream);
-  return varlen ? launch_fp8<false, true>(p, grid, stream) : launch_fp8<false, false>(p, grid, stream);
+  if (causal) return varlen ? launch_fp8_b<true, true>(p, grid, blockscale, stream)
+                            : launch_fp8_b<true, false>(p, grid, blockscale, stream);
+  return varlen ? launch_fp8_b<false, true>(p, grid, blockscale, stream)
+                : launch_fp8_b<false, false>(p, grid, blockscale, stream);
 }
 
 }  // namespace fa

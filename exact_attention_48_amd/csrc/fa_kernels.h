@@ -27,14 +27,18 @@ struct FwdParams {
   int n_splits;
   int chunk;                   // keys per chunk, ceil(Nk / n_splits)
   // 8-bit Q/K (fwd_fp8_launch): q and k hold E4M3 codes, dequantised by these
-  const float* q_descale;      // [B, Hq]
-  const float* k_descale;      // [B, Hkv]
+  const float* q_descale;      // [B, Hq], or [B, Hq, fp8_nb] with block descales
+  const float* k_descale;      // [B, Hkv], or [B, Hkv, fp8_nb]
+  int fp8_nb;                  // block descales: blocks per (sequence, head), ceil(N / kFp8Block)
 };
+
+constexpr int kFp8Block = 64;        // tokens per descale block (local positions 64 j .. 64 j + 63)
+constexpr int kFp8MaxBlocks = 4096;  // block descales: at most this many blocks per (sequence, head)
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream);
 hipError_t fwd_pp_launch(FwdParams p, int causal, int varlen, int expmode, hipStream_t stream);
 hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream);
-hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, hipStream_t stream);
+hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, bool blockscale, hipStream_t stream);
 hipError_t merge_launch(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B,
                         int H, int N, int d, hipStream_t stream);
 

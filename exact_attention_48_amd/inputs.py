@@ -251,12 +251,13 @@ def make_split_inputs(B: int, Nq: int, Nk: int, Hq: int, Hkv: int, d: int, causa
 
 @dataclasses.dataclass
 class Fp8Inputs:
-    """Q, K as E4M3 codes (uint8) with per-(sequence, head) fp32 descales; V as bf16 bits."""
+    """Q, K as E4M3 codes (uint8) with fp32 descales per (sequence, head) or per 64-token
+    block of each (sequence, head); V as bf16 bits."""
     q8: np.ndarray
     k8: np.ndarray
     v: np.ndarray
-    q_descale: np.ndarray        # float32 [B, Hq]
-    k_descale: np.ndarray        # float32 [B, Hkv]
+    q_descale: np.ndarray        # float32 [B, Hq], or [B, Hq, nb] per 64-token block
+    k_descale: np.ndarray        # float32 [B, Hkv], or [B, Hkv, nb]
     cu_seqlens: Optional[np.ndarray]
     B: int
     N: int
@@ -286,9 +287,39 @@ def _quantize_heads(x: np.ndarray, cu: Optional[np.ndarray], nseq: int):
     return codes, ds
 
 
+FP8_SCALE_BLOCK = 64     # tokens per descale block (local positions 64 j .. 64 j + 63)
+
+
+def _quantize_blocks(x: np.ndarray, cu: Optional[np.ndarray], nseq: int, nb: int):
+    """Per-(sequence, head, 64-token block) descale = amax / 448 and the E4M3 codes."""
+    H = x.shape[-2]
+    ds = np.ones((nseq, H, nb), dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    for s in range(nseq):
+        seq = x[s] if cu is None else x[int(cu[s]):int(cu[s + 1])]
+        out = np.zeros(seq.shape, dtype=np.uint8)
+        for j in range(0, seq.shape[0], FP8_SCALE_BLOCK):
+            blk = seq[j:j + FP8_SCALE_BLOCK]
+            amax = np.max(np.abs(blk), axis=(0, 2))                   # [H]
+            d = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+            ds[s, :, j // FP8_SCALE_BLOCK] = d
+            out[j:j + FP8_SCALE_BLOCK] = f32_to_e4m3_bits(blk / d.astype(np.float64)[None, :, None])
+        if cu is None:
+            codes[s] = out
+        else:
+            codes[int(cu[s]):int(cu[s + 1])] = out
+    return codes, ds
+
+
 def make_fp8_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, causal: bool, seed: int,
-                    lengths: Optional[np.ndarray] = None, scale: Optional[float] = None) -> Fp8Inputs:
-    """Q, K, V drawn as for make_inputs; Q and K quantised to E4M3 per (sequence, head), V to bf16."""
+                    lengths: Optional[np.ndarray] = None, scale: Optional[float] = None,
+                    block_scale: bool = False, block_gain: float = 0.0) -> Fp8Inputs:
+    """Q, K, V drawn as for make_inputs; Q and K quantised to E4M3 per (sequence, head), or per
+    64-token block of each (sequence, head) with ``block_scale``; V to bf16. ``block_gain`` g > 0
+    multiplies every 64-token block of Q and K (per head) by 2^-u, u uniform in [0, g], before
+    quantisation: block descales then differ by up to 2^g while the scores only shrink (larger
+    scores would make the softmax peak on single keys, where |O| reaches the largest |V| and
+    bf16's output rounding alone exceeds 1e-2 above |O| = 4)."""
     rng = np.random.default_rng(seed)
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(d)))
@@ -305,8 +336,21 @@ def make_fp8_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, causal: bool, see
     q = rng.standard_normal(qs, dtype=np.float32)
     k = rng.standard_normal(ks, dtype=np.float32)
     v = _draw_bf16(rng, ks)
-    q8, qd = _quantize_heads(q, cu, B)
-    k8, kd = _quantize_heads(k, cu, B)
+    if block_gain > 0:
+        for x in (q, k):
+            for s in range(B):
+                lo, hi = (s * N, s * N + N) if cu is None else (int(cu[s]), int(cu[s + 1]))
+                flat = x.reshape(-1, x.shape[-2], x.shape[-1])
+                for j in range(lo, hi, FP8_SCALE_BLOCK):
+                    g = np.exp2(-rng.uniform(0.0, block_gain, size=x.shape[-2])).astype(np.float32)
+                    flat[j:min(j + FP8_SCALE_BLOCK, hi)] *= g[None, :, None]
+    if block_scale:
+        nb = (N + FP8_SCALE_BLOCK - 1) // FP8_SCALE_BLOCK
+        q8, qd = _quantize_blocks(q, cu, B, nb)
+        k8, kd = _quantize_blocks(k, cu, B, nb)
+    else:
+        q8, qd = _quantize_heads(q, cu, B)
+        k8, kd = _quantize_heads(k, cu, B)
     return Fp8Inputs(q8=q8, k8=k8, v=v, q_descale=qd, k_descale=kd, cu_seqlens=cu, B=B, N=N, Hq=Hq, Hkv=Hkv,
                      d=d, causal=causal, scale=scale)
 

@@ -167,7 +167,8 @@ def merge(o_part, lse_part, stream=None, out=None, lse=None):
 def forward_fp8(q8, k8, v, q_descale, k_descale, causal: bool, scale: Optional[float] = None, cu_seqlens=None,
                 max_seqlen=None, stream=None, options: Optional[capi.FaOptions] = None):
     """8-bit Q/K forward: q8/k8 uint8 E4M3 codes in the Q/K layouts, v bf16, fp32 descales
-    [B, Hq] and [B, Hkv]. Returns (O bf16, LSE fp32)."""
+    [B, Hq] and [B, Hkv] (per sequence and head, fa_fwd_fp8_ex) or [B, Hq, nb] and [B, Hkv, nb]
+    (per 64-token block, nb = ceil(N / 64), fa_fwd_fp8_blockscale). Returns (O bf16, LSE fp32)."""
     _check("q8", q8, torch.uint8)
     _check("k8", k8, torch.uint8)
     _check("v", v)
@@ -176,13 +177,15 @@ def forward_fp8(q8, k8, v, q_descale, k_descale, causal: bool, scale: Optional[f
     B, N, Hq, Hkv, d = _dims(q8, k8, cu_seqlens, max_seqlen)
     if v.shape != k8.shape:
         raise ValueError(f"v has shape {tuple(v.shape)}, expected {tuple(k8.shape)}")
-    _same_shape("q_descale", q_descale, (B, Hq))
-    _same_shape("k_descale", k_descale, (B, Hkv))
+    blocks = q_descale.dim() == 3
+    nb = (N + 63) // 64
+    _same_shape("q_descale", q_descale, (B, Hq, nb) if blocks else (B, Hq))
+    _same_shape("k_descale", k_descale, (B, Hkv, nb) if blocks else (B, Hkv))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse_shape = (B, Hq, N) if cu_seqlens is None else (Hq, q8.shape[0])
     lse = torch.empty(lse_shape, dtype=torch.float32, device=q8.device)
-    capi.fa_fwd_fp8_ex(q8, k8, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens,
-                       options, stream)
+    fn = capi.fa_fwd_fp8_blockscale if blocks else capi.fa_fwd_fp8_ex
+    fn(q8, k8, v, q_descale, k_descale, o, lse, B, Hq, Hkv, N, d, int(causal), scale, cu_seqlens, options, stream)
     return o, lse

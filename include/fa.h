@@ -205,6 +205,31 @@ fa_status fa_fwd_fp8_ex(const void* q, const void* k, const void* v, const float
                         int causal, float softmax_scale, const int32_t* cu_seqlens,
                         const fa_fwd_options* options, void* stream);
 
+/* Tokens per descale block of fa_fwd_fp8_blockscale, and its largest block count. */
+#define FA_FP8_SCALE_BLOCK 64
+#define FA_FP8_MAX_BLOCKS 4096
+
+/*
+ * fa_fwd_fp8 with one descale per block of 64 tokens of every (sequence,
+ * head) instead of one per (sequence, head): finer scaling of the 8-bit
+ * inputs (the low-precision variant of FlashAttention's lineage; podcast.app
+ * episode page, source list). With nb = ceil(N / FA_FP8_SCALE_BLOCK), N the
+ * (maximum) sequence length, the element of token t (position local to its
+ * sequence s) and head h has the value
+ *   q: code * q_descale[s, h, t / 64]      k: code * k_descale[s, hkv, t / 64]
+ *   q_descale  fp32 [B, Hq, nb], device
+ *   k_descale  fp32 [B, Hkv, nb], device
+ * Descales must be finite and > 0. The exp2 factor of each 32-key tile is
+ * softmax_scale * log2(e) times the query's and the tile's descales, folded in
+ * once per tile; the result is the exact attention of the dequantised Q and
+ * K. Returns FA_ERR_UNSUPPORTED when nb > FA_FP8_MAX_BLOCKS (N > 262144) or
+ * d != 128; options, other arguments and errors as for fa_fwd_fp8_ex.
+ */
+fa_status fa_fwd_fp8_blockscale(const void* q, const void* k, const void* v, const float* q_descale,
+                                const float* k_descale, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                                int d, int causal, float softmax_scale, const int32_t* cu_seqlens,
+                                const fa_fwd_options* options, void* stream);
+
 /*
  * Split-KV partial attention (uniform batches). The keys of every sequence are
  * cut into n_splits contiguous chunks of C = ceil(Nk / n_splits) keys (chunk p:

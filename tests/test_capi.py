@@ -191,6 +191,27 @@ def test_fp8_rejects(lib, kw, expect):
     assert fp8(**kw) == expect
 
 
+def fp8_blocks(*, q=A, k=A, v=A, qd=A, kd=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, scale=0.1,
+               cu=None, opt=None):
+    return capi.fa_fwd_fp8_blockscale(q, k, v, qd, kd, o, lse, B, Hq, Hkv, N, d, causal, scale, cu, opt, stream=0,
+                                      check=False)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=64 * 4096 + 1), capi.FA_ERR_UNSUPPORTED),         # more than 4096 descale blocks
+    (dict(N=64 * 4096 + 1, B=0), capi.FA_ERR_UNSUPPORTED),    # the block limit comes before the empty check
+    (dict(d=64), capi.FA_ERR_UNSUPPORTED),
+    (dict(qd=None), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(kd=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), capi.FA_ERR_INVALID_ARGUMENT),
+    (dict(opt=capi.FaOptions(capi.FA_EXP_POLY, 8.0, 1)), capi.FA_ERR_UNSUPPORTED),
+    (dict(B=0), capi.FA_OK),
+    (dict(N=0), capi.FA_OK),
+])
+def test_fp8_blockscale_rejects(lib, kw, expect):
+    assert fp8_blocks(**kw) == expect
+
+
 def exp2_eval(*, x=A, y=A + 4096, n=16, mode=capi.FA_EXP_HW):
     return capi.fa_exp2_eval(x, y, n, mode, stream=0, check=False)
 
