@@ -21,23 +21,26 @@
 //                and O^T += V_{i-1}^T P_{i-1}^T (16 MFMAs, P from registers,
 //                V^T through the transposing ds_read_b64_tr_b16);
 //   SOFTMAX(i) : P_i = exp2(S_i c - m c), row sums, bf16 pack (vector only).
-// The phases of the whole workgroup are separated by barriers, and group B
-// runs one phase behind group A, so in every phase one wave of each SIMD is
-// in a GEMM phase and the other in a softmax phase:
-//   phase 2i   : A GEMM(i-1)      B SOFTMAX(i-1)
-//   phase 2i+1 : A SOFTMAX(i)     B GEMM(i-1)
-// The GEMM wave raises its priority (s_setprio) so the arbiter issues its
-// MFMAs first and the softmax wave fills the remaining issue slots.
+// Group B runs one phase behind group A. The workgroup synchronises once per
+// slot of two phases, and the two groups take the slot's phases in opposite
+// orders, so that one wave of each SIMD is in a GEMM phase while the other is
+// in a softmax phase:
+//   slot i : A  GEMM(i-1), SOFTMAX(i)      B  SOFTMAX(i-1), GEMM(i-1)
+// (one barrier per slot measured 2-5 % faster than one per phase: the
+// order of the code keeps the groups apart, and half the barriers go). The
+// GEMM wave raises its priority (s_setprio) so the arbiter issues its MFMAs
+// first and the softmax wave fills the remaining issue slots.
 //
 // Tile copies (HBM -> LDS without register staging, buffer_load ... lds) go out
 // from the softmax phases only, one 1 KiB instruction per 16 exponentials: a
 // copy instruction holds its wave at issue for about 65-100 clocks (measured),
-// which in a GEMM phase would stall the MFMA stream. Group A issues its share of
-// tile i+2 in its SOFTMAX(i) (phase 2i+1), group B its share of tile i+3 in its
-// SOFTMAX(i) (phase 2i+2); at the end of phase 2i+1 every wave waits for its
-// share of tile i+1, and the barrier makes the whole tile visible before A
-// reads it at phase 2i+2. The GEMM phase starts with the P V MFMAs, whose first
-// V^T fragments the wave read at the end of its softmax phase.
+// which in a GEMM phase would stall the MFMA stream. In slot i both groups
+// issue their shares of tile i+2 (A in SOFTMAX(i), B in SOFTMAX(i-1)), into the
+// stage of tile i-2, which the slots before last read; at the end of slot i
+// every wave waits for its share of tile i+1, and the barrier makes the whole
+// tile visible before slot i+1 reads it. The GEMM phase starts with the P V
+// MFMAs, whose first V^T fragments the wave read at the end of its softmax
+// phase.
 //
 // LDS layout and addressing: one 128 KiB array, the 4 V stages in its lower
 // 64 KiB and the 4 K stages in the upper 64 KiB, 16 KiB each. Every fragment
@@ -364,13 +367,14 @@ void fa_fwd_pp_kernel(const FwdParams p) {
 
   // ---- the phase loop of one pass ----
   // Every wave runs the same sequence of actions, GEMM(-1), SOFTMAX(0),
-  // GEMM(0), SOFTMAX(1), ..., SOFTMAX(n_t-1), GEMM(n_t-1), one per phase;
-  // group B runs it one phase behind group A (B is idle in phase 0, A in the
-  // last phase). GEMM(k-1) computes S_k (k < n_t) and O += V_{k-1} P_{k-1}
-  // (k >= 1). Copies and waits follow the global phase: at the start of each
-  // even phase 2j every wave issues tile j+2; at the end of each odd phase
-  // 2j+1 it waits for tile j+1 (tile j+2 may stay in flight).
-  auto wait_tile = [&](const int j) __attribute__((always_inline)) {   // end of phase 2j+1
+  // GEMM(0), SOFTMAX(1), ..., SOFTMAX(n_t-1), GEMM(n_t-1); group B runs it one
+  // phase behind group A. GEMM(k-1) computes S_k (k < n_t) and O += V_{k-1}
+  // P_{k-1} (k >= 1). The two prologue phases have a barrier each; after them
+  // A synchronises after each SOFTMAX(k) and B after each GEMM(k-1), which
+  // makes slot k = {A: GEMM(k-1), SOFTMAX(k); B: SOFTMAX(k-1), GEMM(k-1)}
+  // (both groups pass the same number of barriers). At the end of slot j each
+  // wave waits for its share of tile j+1 (tile j+2 may stay in flight).
+  auto wait_tile = [&](const int j) __attribute__((always_inline)) {   // end of slot j
     if (j + 2 < n_t) wait_vm(OPS);
     else if (j + 1 < n_t) wait_vm(0);
   };
@@ -383,23 +387,27 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // V_{k-1} in the stage before it. The GEMM waves issue no copies (a copy
   // instruction would hold the MFMA stream); each wave issues its share of a
   // tile from its softmax phase, between the exponentials: group A in
-  // SOFTMAX(k) (phase 2k+1) tile k+2, group B in SOFTMAX(k) (phase 2k+2) tile
-  // k+3, each into the stage of a tile whose last reader finished before (tile
-  // k-2: B's GEMM at phase 2k-1; tile k-1: B's GEMM at phase 2k+1). At the end
-  // of SOFTMAX(k) the wave reads the first V^T fragments of its next GEMM (V_k).
+  // SOFTMAX(k) (slot k) tile k+2, group B in SOFTMAX(k) (slot k+1) tile k+3,
+  // each into the stage of the tile two before it, whose last readers were the
+  // GEMMs of the slot before. At the end of SOFTMAX(k) the wave reads the first
+  // V^T fragments of its next GEMM (V_k).
   auto pair = [&](auto bi_tag, const int k, const int pass, bf16x8 (&pre)[PP_PF]) __attribute__((always_inline)) {
     constexpr int BI = decltype(bi_tag)::value;
     gemm(ic<1>{}, ic<1>{}, ic<BI>{}, ic<(BI + 3) % 4>{}, pre);
     __builtin_amdgcn_sched_barrier(0);
-    if (!grp_a) wait_tile(k);                   // B: phase 2k+1 is odd
-    sync();
+    if (!grp_a) {                               // B: end of slot k
+      wait_tile(k);
+      sync();
+    }
     const bool cp = grp_a ? k + 2 < n_t : k + 3 < n_t;
     if (cp) begin_copy(grp_a ? (BI + 2) % 4 : (BI + 3) % 4);
     softmax(k, pass, cp);
     prefetch_v(pre, ic<BI>{});
     __builtin_amdgcn_sched_barrier(0);
-    if (grp_a) wait_tile(k);                    // A: phase 2k+1 is odd
-    sync();
+    if (grp_a) {                                // A: end of slot k
+      wait_tile(k);
+      sync();
+    }
   };
   auto run_pass = [&](const int pass) __attribute__((always_inline)) {
     bf16x8 pre[PP_PF];
@@ -419,14 +427,13 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     wait_tile(0);
     sync();
-    // phase 2 for B: SOFTMAX(0) with its share of tile 3, then V_0's first
-    // fragments. The pairs k = 1 .. n_t - 1 then run from each wave's own
-    // point of view, B one phase behind A.
+    // B's SOFTMAX(0), with its share of tile 3, then V_0's first fragments,
+    // opens slot 1 (no barrier before B's GEMM(0)). The pairs k = 1 .. n_t - 1
+    // then run from each wave's own point of view, B one phase behind A.
     if (!grp_a) {
       if (3 < n_t) begin_copy(3);
       softmax(0, pass, 3 < n_t);
       prefetch_v(pre, ic<0>{});
-      sync();
     }
     int k = 1;
     for (; k + 3 < n_t; k += 4) {
@@ -453,9 +460,7 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       vaddr[db][1] -= vshift;
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (!grp_a) wait_tile(n_t);
-    sync();
-    if (grp_a) sync();                          // A's idle last phase (B's last GEMM)
+    sync();                                     // the last slot: both groups' GEMM(n_t-1)
   };
 
   const float l_limit = exp2f(tau);
