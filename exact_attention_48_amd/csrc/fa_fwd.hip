@@ -634,6 +634,7 @@ hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, h
 }
 
 hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream) {
+  if (d == 128) return fwd_pp_split_launch(p, causal, stream);   // two waves per SIMD (fa_fwd_pp.hip)
   p.n_qtiles = (p.N + BM - 1) / BM;
   const long grid_l = q_grid_level(p.B * p.n_splits, p.Hq, p.G, p.n_qtiles);
   if (grid_l == 0) return hipSuccess;

@@ -81,9 +81,13 @@ constexpr int PP_PF = 4;                     // operand fragments read ahead
 
 }  // namespace
 
-template <bool CAUSAL, bool VARLEN, int EXPMODE>
+// SPLIT: split-KV partial results (uniform batches): work item (sequence,
+// key chunk, query head, query tile) over the chunk's keys [kbeg, kend) only,
+// query i at key position i + q_off for the causal mask, fp32 O_p and LSE_p out.
+template <bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS), amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_pp_kernel(const FwdParams p) {
+  static_assert(!(SPLIT && VARLEN), "split-KV partial results are for uniform batches");
   constexpr int D = PP_D;
   constexpr int BN = PP_BN;
   constexpr int KSTEPS = D / 16;              // S^T k-steps
@@ -107,29 +111,40 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   if constexpr (VARLEN) {
     if (!q_item_xcd(blockIdx.x, p.B, p.Hkv, p.G, p.kv_chunks, p.n_qtiles, p.lpt, item)) return;
   } else {
-    if (!q_item_level(blockIdx.x, p.B, p.Hq, p.G, p.n_qtiles, p.lpt, item)) return;
+    if (!q_item_level(blockIdx.x, SPLIT ? p.B * p.n_splits : p.B, p.Hq, p.G, p.n_qtiles, p.lpt, item)) return;
   }
-  const int s = item.s, h = item.h, qt = item.t;
+  const int s = SPLIT ? item.s / p.n_splits : item.s;
+  const int sp = SPLIT ? item.s - s * p.n_splits : 0;
+  const int h = item.h, qt = item.t;
   const int hkv = h / p.G;
-  int seq0, L;
+  int seq0, L, kseq0, Lk;                     // queries: rows seq0.., L of them; keys: kseq0.., Lk
   if constexpr (VARLEN) {
     seq0 = p.cu_seqlens[s];
     L = p.cu_seqlens[s + 1] - seq0;
+    kseq0 = seq0;
+    Lk = L;
   } else {
     seq0 = s * p.N;
     L = p.N;
+    kseq0 = SPLIT ? s * p.Nk : seq0;
+    Lk = SPLIT ? p.Nk : L;
   }
+  // keys of this work item: [kbeg, kend) (a split call's chunk); query i sits
+  // at key position i + q_off for the causal mask
+  const int q_off = SPLIT ? p.q_off : 0;
+  const int kbeg = SPLIT ? min(sp * p.chunk, Lk) : 0;
+  const int kend = SPLIT ? (int)min((long)(sp + 1) * p.chunk, (long)Lk) : Lk;
   const int q0 = qt * PP_BM;
   if (q0 >= L) return;
   const int qw0 = q0 + wave * PP_WQ;          // first query of this wave
   const int my_q = qw0 + l32;
-  const int kv_end = CAUSAL ? min(L, q0 + PP_BM) : L;
-  const int n_t = (kv_end + BN - 1) / BN;     // key tiles of the workgroup (>= 1)
+  const int kv_end = CAUSAL ? min(kend, q0 + PP_BM + q_off) : kend;
+  const int n_t = kv_end > kbeg ? (kv_end - kbeg + BN - 1) / BN : 0;   // key tiles (>= 1 unless SPLIT)
 
   const long q_row_stride = (long)p.Hq * D;
   const long kv_stride = (long)p.Hkv * D * 2; // bytes per token row of K and V
-  const char* kbase = (const char*)p.k + ((long)seq0 * p.Hkv + hkv) * D * 2;
-  const char* vbase = (const char*)p.v + ((long)seq0 * p.Hkv + hkv) * D * 2;
+  const char* kbase = (const char*)p.k + ((long)(kseq0 + kbeg) * p.Hkv + hkv) * D * 2;
+  const char* vbase = (const char*)p.v + ((long)(kseq0 + kbeg) * p.Hkv + hkv) * D * 2;
 
   // ---- Q fragments (B operands of S^T = K Q^T): query my_q, d = 16 ks + 8 hl .. + 7 ----
   bf16x8 qf[KSTEPS];
@@ -180,11 +195,11 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     c_mv = m_wave + (unsigned)(VREG + stage * PP_TILEB);
     c_rk = rsrc_of(kcur);
     c_rv = rsrc_of(vcur);
-    if (r0 + BN <= L) {
+    if (kbeg + r0 + BN <= kend) {
       c_off[0] = coff[0];
       c_off[1] = coff[1];
     } else {
-      const int last = L - 1 - r0;
+      const int last = kend - 1 - kbeg - r0;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = min(crow0 + 4 * u, last);
@@ -294,18 +309,19 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- softmax phase of tile i (keys k0 = 64 i ..), S^T in sacc ----
+  // ---- softmax phase of tile i (keys k0 = kbeg + 64 i ..), S^T in sacc ----
   // element (kb, r): key k0 + 32 kb + 8 (r / 4) + 4 hl + r % 4, query my_q
   auto needs_mask = [&](int k0) __attribute__((always_inline)) {
-    return (k0 + BN > L) || (CAUSAL && k0 + BN - 1 > qw0);
+    return (k0 + BN > kend) || (CAUSAL && k0 + BN - 1 > qw0 + q_off);
   };
-  // Masked elements: key >= L, or (causal) key > my_q. With kl = k0 + 4 hl (this
-  // lane's first key of the tile) and element offset e = 32 kb + 8 (r / 4) + r % 4,
-  // element e is dead iff e >= thr, thr = min(L, my_q + 1) - kl (one register per
-  // tile); each element is then one compare into VCC and one select.
+  // Masked elements: key >= kend, or (causal) key > my_q + q_off. With kl = k0 +
+  // 4 hl (this lane's first key of the tile) and element offset e = 32 kb +
+  // 8 (r / 4) + r % 4, element e is dead iff e >= thr, thr = min(kend, my_q +
+  // q_off + 1) - kl (one register per tile); each element is then one compare
+  // into VCC and one select.
   auto mask_tile = [&](int k0) __attribute__((always_inline)) {
     const int kl = k0 + 4 * hl;
-    const int thr = (CAUSAL ? min(L, my_q + 1) : L) - kl;
+    const int thr = (CAUSAL ? min(kend, my_q + q_off + 1) : kend) - kl;
     const float ninf = -INFINITY;
     static_for<0, 32>([&](auto e_tag) __attribute__((always_inline)) {
       constexpr int kb = decltype(e_tag)::value >> 4, r = decltype(e_tag)::value & 15;
@@ -352,7 +368,7 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // `copy`: the four copy instructions of the tile begun by begin_copy go out
   // before the exponentials
   auto softmax = [&](int i, int pass, const bool copy) __attribute__((always_inline)) {
-    const int k0 = i * BN;
+    const int k0 = kbeg + i * BN;
     if (needs_mask(k0)) mask_tile(k0);
     if (pass == 1) {                           // tracking pass: the true row maxima only
       m_seen = vmax(m_seen, tile_max());
@@ -468,7 +484,12 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   };
 
   const float l_limit = exp2f(tau);
-  for (int pass = 0;; ++pass) {
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+  m_run = -INFINITY;
+  // a split work item whose chunk holds no key its queries see: O_p = 0, LSE_p = -inf
+  // (n_t is uniform over the workgroup, so no wave skips a barrier the others take)
+  for (int pass = 0; n_t > 0; ++pass) {
     iss = 0;
     kcur = kbase;
     vcur = vbase;
@@ -506,6 +527,20 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   }
 
   // ---- epilogue: O = O / l (bf16, staged through LDS), LSE = ln 2 (m c + log2 l) ----
+  if constexpr (SPLIT) {
+    // fp32 O_p rows straight from the accumulators; rows that saw no key of the
+    // chunk hold O_p = 0, LSE_p = -inf
+    const long part = (long)sp * p.B + s;
+    float* ob = p.o_part + (part * p.N * p.Hq + h) * D;
+    const float l_tot = pair_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    store_rows_f32<D>(oacc, inv, ob, q_row_stride, qw0, L, lane);
+    if (hl == 0 && my_q < L) {
+      const float lse = (m_run == -INFINITY || l_tot == 0.f) ? -INFINITY : (m_run * c + __log2f(l_tot)) * kLn2;
+      p.lse_part[(part * p.Hq + h) * p.N + my_q] = lse;
+    }
+    return;
+  }
   char FA_LDS* st = (char FA_LDS*)lds + wave * PP_TILEB;   // this wave's output staging (16 KiB)
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -520,9 +555,9 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   }
 }
 
-template <bool CAUSAL, bool VARLEN, int EXPMODE>
+template <bool CAUSAL, bool VARLEN, int EXPMODE, bool SPLIT = false>
 static hipError_t launch_pp(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, VARLEN, EXPMODE>), dim3(grid), dim3(PP_THREADS), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<CAUSAL, VARLEN, EXPMODE, SPLIT>), dim3(grid), dim3(PP_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -543,6 +578,17 @@ hipError_t fwd_pp_launch(FwdParams p, int causal, int varlen, int expmode, hipSt
                             : launch_pp_e<true, false>(p, grid, expmode, stream);
   return varlen ? launch_pp_e<false, true>(p, grid, expmode, stream)
                 : launch_pp_e<false, false>(p, grid, expmode, stream);
+}
+
+// d = 128 split-KV partial results (uniform batches): the two-waves-per-SIMD
+// kernel over (sequence, key chunk) work items.
+hipError_t fwd_pp_split_launch(FwdParams p, int causal, hipStream_t stream) {
+  p.n_qtiles = (p.N + PP_BM - 1) / PP_BM;
+  const long grid_l = q_grid_level(p.B * p.n_splits, p.Hq, p.G, p.n_qtiles);
+  if (grid_l == 0) return hipSuccess;
+  if (grid_l > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const int grid = (int)grid_l;
+  return causal ? launch_pp<true, false, 0, true>(p, grid, stream) : launch_pp<false, false, 0, true>(p, grid, stream);
 }
 
 }  // namespace fa

@@ -37,6 +37,7 @@ constexpr int kFp8MaxBlocks = 4096;  // block descales: at most this many blocks
 
 hipError_t fwd_launch(FwdParams p, int d, int causal, int varlen, int expmode, hipStream_t stream);
 hipError_t fwd_pp_launch(FwdParams p, int causal, int varlen, int expmode, hipStream_t stream);
+hipError_t fwd_pp_split_launch(FwdParams p, int causal, hipStream_t stream);
 hipError_t fwd_split_launch(FwdParams p, int d, int causal, hipStream_t stream);
 hipError_t fwd_fp8_launch(FwdParams p, int causal, int varlen, bool blockscale, hipStream_t stream);
 hipError_t merge_launch(const float* o_part, const float* lse_part, void* o, float* lse, int n_parts, int B,
