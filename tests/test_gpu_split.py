@@ -18,6 +18,9 @@ SPLIT_CASES = [
     (1, 64, 64, 2, 1, 128, True, 9),        # 8-key chunks; early rows see nothing of later chunks
     (1, 33, 40, 2, 2, 64, False, 16),       # 3-key chunks: the last two chunks are empty
     (1, 520, 4100, 4, 4, 128, True, 1),     # one chunk: plain attention in fp32 partial form
+    (1, 33, 40, 2, 2, 128, False, 16),      # d = 128 with empty trailing chunks
+    (1, 300, 100, 2, 1, 128, False, 3),     # more queries than keys (no mask)
+    (2, 600, 1300, 4, 2, 128, True, 5),     # three query tiles, causal offset 700 across 260-key chunks
 ]
 
 
