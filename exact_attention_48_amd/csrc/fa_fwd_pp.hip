@@ -346,7 +346,7 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // per tile but puts the bf16 rounding of P into l: rows with few keys then
   // miss the 1e-3 LSE tolerance.)
   auto exps = [&](const bool copy) __attribute__((always_inline)) {
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+    float lp[4];                                 // four row-sum chains, each from its first term
     if (copy) {                                  // the tile's four copy instructions first
 #pragma unroll
       for (int part = 0; part < 4; ++part) copy_part(part);
@@ -358,7 +358,8 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       for (int e = 0; e < 8; e += 2) {
         const float p0 = exp2_sel<EXPMODE>(__builtin_fmaf(sacc[kb][r0 + e], c, -mc));
         const float p1 = exp2_sel<EXPMODE>(__builtin_fmaf(sacc[kb][r0 + e + 1], c, -mc));
-        lp[e >> 1] += p0;
+        if (t == 0) lp[e >> 1] = p0;           // (not 0 + p0: that add is not folded away)
+        else lp[e >> 1] += p0;
         lp[e >> 1] += p1;
         pb[t][e >> 1] = __builtin_bit_cast(unsigned, pack_bf16(p0, p1));
       }
