@@ -167,8 +167,6 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   }
   const unsigned m_wave = lds0 + (unsigned)wave * 2048u;   // this wave's first 1 KiB row group in a stage
   int iss = 0;                                // next tile to copy
-  const char* kcur = kbase;
-  const char* vcur = vbase;
   // one 16-byte-per-lane HBM -> LDS load: M0 = LDS address of lane 0's 16 bytes
   auto rsrc_of = [&](const char* base) __attribute__((always_inline)) {
     const unsigned long long a64 = (unsigned long long)base;
@@ -179,22 +177,29 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     r[3] = 0x00020000u;
     return r;
   };
-  auto dma = [&](const u32x4& rsrc, unsigned voff, unsigned m0v) __attribute__((always_inline)) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0v), "v"(voff), "s"(rsrc) : "memory", "m0");
+  auto dma = [&](const u32x4& rsrc, unsigned voff, unsigned soff, unsigned m0v) __attribute__((always_inline)) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
   };
   // A tile copy in four single instructions (K rows u = 0, V rows u = 0, K rows
   // u = 1, V rows u = 1), so that a wave can spread them over its softmax work:
   // an HBM -> LDS load instruction holds its wave at issue for tens of clocks
   // while the CU's vector-memory path takes its 1 KiB.
   u32x4 c_rk, c_rv;
-  unsigned c_mk, c_mv, c_off[2];
+  unsigned c_mk, c_mv, c_so, c_off[2];
   auto begin_copy = [&](const int stage) __attribute__((always_inline)) {
     const int r0 = iss * BN;
     c_mk = m_wave + (unsigned)(KREG + stage * PP_TILEB);
     c_mv = m_wave + (unsigned)(VREG + stage * PP_TILEB);
-    c_rk = rsrc_of(kcur);
-    c_rv = rsrc_of(vcur);
+    // Loop-invariant K and V descriptors, rebased every 256 tiles, plus a
+    // scalar offset per tile: the per-tile 64-bit pointer updates would sit in
+    // vector registers (the scalar file is nearly full) and cost six vector
+    // instructions of the softmax phase per tile.
+    if ((iss & 255) == 0) {
+      c_rk = rsrc_of(kbase + (long)r0 * kv_stride);
+      c_rv = rsrc_of(vbase + (long)r0 * kv_stride);
+    }
+    c_so = (unsigned)((iss & 255) * BN) * (unsigned)kv_stride;   // < 256 * 64 rows of one window
     if (kbeg + r0 + BN <= kend) {
       c_off[0] = coff[0];
       c_off[1] = coff[1];
@@ -207,14 +212,12 @@ void fa_fwd_pp_kernel(const FwdParams p) {
                    (unsigned)(((lane & 15) ^ lds_swz<D>(crow0 + 4 * u)) * 16);
       }
     }
-    kcur += BN * kv_stride;
-    vcur += BN * kv_stride;
     ++iss;
   };
   auto copy_part = [&](const int part) __attribute__((always_inline)) {
     const int u = part >> 1;
-    if (part & 1) dma(c_rv, c_off[u], c_mv + 1024u * u);
-    else dma(c_rk, c_off[u], c_mk + 1024u * u);
+    if (part & 1) dma(c_rv, c_off[u], c_so, c_mv + 1024u * u);
+    else dma(c_rk, c_off[u], c_so, c_mk + 1024u * u);
   };
   auto issue_tile = [&](const int stage) __attribute__((always_inline)) {
     begin_copy(stage);
@@ -492,8 +495,6 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // (n_t is uniform over the workgroup, so no wave skips a barrier the others take)
   for (int pass = 0; n_t > 0; ++pass) {
     iss = 0;
-    kcur = kbase;
-    vcur = vbase;
     issue_tile(0);
     if (n_t > 1) issue_tile(1);
 #pragma unroll

@@ -21,6 +21,7 @@ SPLIT_CASES = [
     (1, 33, 40, 2, 2, 128, False, 16),      # d = 128 with empty trailing chunks
     (1, 300, 100, 2, 1, 128, False, 3),     # more queries than keys (no mask)
     (2, 600, 1300, 4, 2, 128, True, 5),     # three query tiles, causal offset 700 across 260-key chunks
+    (1, 64, 20000, 2, 1, 128, True, 1),     # one chunk of 313 key tiles (past a 256-tile copy window)
 ]
 
 
