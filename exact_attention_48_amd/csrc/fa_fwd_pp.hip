@@ -33,15 +33,15 @@
 //
 // Tile copies (HBM -> LDS without register staging, buffer_load ... lds) go out
 // from the softmax phases only, the four 1 KiB instructions of a wave's share
-// at the start of the phase (measured 0.4 % faster than one per 16
+// just before the phase's exponentials (measured 0.4 % faster than one per 16
 // exponentials): a copy instruction holds its wave at issue for about 65-100
-// clocks (measured), which in a GEMM phase would stall the MFMA stream. In slot i both groups
-// issue their shares of tile i+2 (A in SOFTMAX(i), B in SOFTMAX(i-1)), into the
-// stage of tile i-2, which the slots before last read; at the end of slot i
-// every wave waits for its share of tile i+1, and the barrier makes the whole
-// tile visible before slot i+1 reads it. The GEMM phase starts with the P V
-// MFMAs, whose first V^T fragments the wave read at the end of its softmax
-// phase.
+// clocks (measured), which in a GEMM phase would stall the MFMA stream. In slot
+// i both groups issue their shares of tile i+2 (A before SOFTMAX(i), B before
+// SOFTMAX(i-1)), into the stage of tile i-2, which the slots before last read;
+// at the end of slot i every wave waits for its share of tile i+1, and the
+// barrier makes the whole tile visible before slot i+1 reads it. The GEMM phase
+// starts with the P V MFMAs, whose first V^T fragments the wave read at the end
+// of its softmax phase.
 //
 // LDS layout and addressing: one 128 KiB array, the 4 V stages in its lower
 // 64 KiB and the 4 K stages in the upper 64 KiB, 16 KiB each. Every fragment
@@ -181,10 +181,10 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
   };
-  // A tile copy in four single instructions (K rows u = 0, V rows u = 0, K rows
-  // u = 1, V rows u = 1), so that a wave can spread them over its softmax work:
-  // an HBM -> LDS load instruction holds its wave at issue for tens of clocks
-  // while the CU's vector-memory path takes its 1 KiB.
+  // A wave's share of a tile copy is four instructions (K rows u = 0, V rows
+  // u = 0, K rows u = 1, V rows u = 1); an HBM -> LDS load instruction holds its
+  // wave at issue for tens of clocks while the CU's vector-memory path takes its
+  // 1 KiB.
   u32x4 c_rk, c_rv;
   unsigned c_mk, c_mv, c_so, c_off[2];
   auto begin_copy = [&](const int stage) __attribute__((always_inline)) {
@@ -348,12 +348,8 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // the rounded bf16 pairs instead, with v_dot2c_f32_bf16, saves 16 instructions
   // per tile but puts the bf16 rounding of P into l: rows with few keys then
   // miss the 1e-3 LSE tolerance.)
-  auto exps = [&](const bool copy) __attribute__((always_inline)) {
+  auto exps = [&]() __attribute__((always_inline)) {
     float lp[4];                                 // four row-sum chains, each from its first term
-    if (copy) {                                  // the tile's four copy instructions first
-#pragma unroll
-      for (int part = 0; part < 4; ++part) copy_part(part);
-    }
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const int kb = t >> 1, r0 = 8 * (t & 1);
@@ -369,24 +365,19 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     }
     l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
   };
-  // `copy`: the four copy instructions of the tile begun by begin_copy go out
-  // before the exponentials
-  auto softmax = [&](int i, int pass, const bool copy) __attribute__((always_inline)) {
+  // (the callers issue the phase's copy instructions just before it)
+  auto softmax = [&](int i, int pass) __attribute__((always_inline)) {
     const int k0 = kbeg + i * BN;
     if (needs_mask(k0)) mask_tile(k0);
     if (pass == 1) {                           // tracking pass: the true row maxima only
       m_seen = vmax(m_seen, tile_max());
-      if (copy) {
-#pragma unroll
-        for (int part = 0; part < 4; ++part) copy_part(part);
-      }
       return;
     }
     if (i == 0 && pass == 0) {                 // the first tile fixes m for the pass
       m_run = tile_max();
       mc = m_run == -INFINITY ? 0.f : m_run * c;
     }
-    exps(copy);
+    exps();
   };
 
   // ---- the phase loop of one pass ----
@@ -424,8 +415,8 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       sync();
     }
     const bool cp = grp_a ? k + 2 < n_t : k + 3 < n_t;
-    if (cp) begin_copy(grp_a ? (BI + 2) % 4 : (BI + 3) % 4);
-    softmax(k, pass, cp);
+    if (cp) issue_tile(grp_a ? (BI + 2) % 4 : (BI + 3) % 4);   // one branch, the copies first
+    softmax(k, pass);
     prefetch_v(pre, ic<BI>{});
     __builtin_amdgcn_sched_barrier(0);
     if (grp_a) {                                // A: end of slot k
@@ -442,8 +433,8 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     // phase 1: A SOFTMAX(0) with its share of tile 2, then V_0's first
     // fragments; B GEMM(-1) = S_0
     if (grp_a) {
-      if (2 < n_t) begin_copy(2);
-      softmax(0, pass, 2 < n_t);
+      if (2 < n_t) issue_tile(2);
+      softmax(0, pass);
       prefetch_v(pre, ic<0>{});
     } else {
       gemm(ic<1>{}, ic<0>{}, ic<0>{}, ic<0>{}, pre);
@@ -455,8 +446,8 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     // opens slot 1 (no barrier before B's GEMM(0)). The pairs k = 1 .. n_t - 1
     // then run from each wave's own point of view, B one phase behind A.
     if (!grp_a) {
-      if (3 < n_t) begin_copy(3);
-      softmax(0, pass, 3 < n_t);
+      if (3 < n_t) issue_tile(3);
+      softmax(0, pass);
       prefetch_v(pre, ic<0>{});
     }
     int k = 1;
