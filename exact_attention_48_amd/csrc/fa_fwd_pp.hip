@@ -186,11 +186,10 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // wave at issue for tens of clocks while the CU's vector-memory path takes its
   // 1 KiB.
   u32x4 c_rk, c_rv;
-  unsigned c_mk, c_mv, c_so, c_off[2];
-  auto begin_copy = [&](const int stage) __attribute__((always_inline)) {
+  auto issue_tile = [&](const int stage) __attribute__((always_inline)) {
     const int r0 = iss * BN;
-    c_mk = m_wave + (unsigned)(KREG + stage * PP_TILEB);
-    c_mv = m_wave + (unsigned)(VREG + stage * PP_TILEB);
+    const unsigned mk = m_wave + (unsigned)(KREG + stage * PP_TILEB);
+    const unsigned mv = m_wave + (unsigned)(VREG + stage * PP_TILEB);
     // Loop-invariant K and V descriptors, rebased every 256 tiles, plus a
     // scalar offset per tile: the per-tile 64-bit pointer updates would sit in
     // vector registers (the scalar file is nearly full) and cost six vector
@@ -199,30 +198,25 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       c_rk = rsrc_of(kbase + (long)r0 * kv_stride);
       c_rv = rsrc_of(vbase + (long)r0 * kv_stride);
     }
-    c_so = (unsigned)((iss & 255) * BN) * (unsigned)kv_stride;   // < 256 * 64 rows of one window
-    if (kbeg + r0 + BN <= kend) {
-      c_off[0] = coff[0];
-      c_off[1] = coff[1];
-    } else {
+    const unsigned so = (unsigned)((iss & 255) * BN) * (unsigned)kv_stride;   // < 256 * 64 rows of one window
+    ++iss;
+    if (kbeg + r0 + BN <= kend) {               // a full tile: the precomputed row offsets
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        dma(c_rk, coff[u], so, mk + 1024u * u);
+        dma(c_rv, coff[u], so, mv + 1024u * u);
+      }
+    } else {                                    // the last tile: rows past the end repeat the last row
       const int last = kend - 1 - kbeg - r0;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = min(crow0 + 4 * u, last);
-        c_off[u] = (unsigned)r * (unsigned)kv_stride +   // chunk order of the LDS row
-                   (unsigned)(((lane & 15) ^ lds_swz<D>(crow0 + 4 * u)) * 16);
+        const unsigned toff = (unsigned)r * (unsigned)kv_stride +   // chunk order of the LDS row
+                              (unsigned)(((lane & 15) ^ lds_swz<D>(crow0 + 4 * u)) * 16);
+        dma(c_rk, toff, so, mk + 1024u * u);
+        dma(c_rv, toff, so, mv + 1024u * u);
       }
     }
-    ++iss;
-  };
-  auto copy_part = [&](const int part) __attribute__((always_inline)) {
-    const int u = part >> 1;
-    if (part & 1) dma(c_rv, c_off[u], c_so, c_mv + 1024u * u);
-    else dma(c_rk, c_off[u], c_so, c_mk + 1024u * u);
-  };
-  auto issue_tile = [&](const int stage) __attribute__((always_inline)) {
-    begin_copy(stage);
-#pragma unroll
-    for (int part = 0; part < 4; ++part) copy_part(part);
   };
 
   // ---- per-lane LDS read bases (byte addresses, opaque to the compiler) ----
@@ -371,6 +365,12 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     if (needs_mask(k0)) mask_tile(k0);
     if (pass == 1) {                           // tracking pass: the true row maxima only
       m_seen = vmax(m_seen, tile_max());
+      // P and l are not used in this pass. Defining them here too lets the
+      // exponentials of the other passes land in P's own registers (otherwise
+      // the merge of the two branches costs nine register moves per tile).
+#pragma unroll
+      for (int t = 0; t < KT; ++t) pb[t] = u32x4{0u, 0u, 0u, 0u};
+      l_run = 0.f;
       return;
     }
     if (i == 0 && pass == 0) {                 // the first tile fixes m for the pass
