@@ -186,6 +186,13 @@ void fa_fwd_pp_kernel(const FwdParams p) {
   // wave at issue for tens of clocks while the CU's vector-memory path takes its
   // 1 KiB.
   u32x4 c_rk, c_rv;
+  // After the last S^T MFMA of a GEMM phase the softmax reads sacc only 19
+  // wait states later. A tile's four copy triples (s_mov m0, s_nop 0, load)
+  // give 12 by themselves; s_nop 7 adds 8 more. Without copies the softmax
+  // waits the full mfma_result_wait().
+  auto copies_then_result_wait = [&]() __attribute__((always_inline)) {
+    asm volatile("s_nop 7" ::: "memory");
+  };
   auto issue_tile = [&](const int stage) __attribute__((always_inline)) {
     const int r0 = iss * BN;
     const unsigned mk = m_wave + (unsigned)(KREG + stage * PP_TILEB);
@@ -302,7 +309,6 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (S) mfma_result_wait();       // the softmax reads sacc next
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -415,7 +421,13 @@ void fa_fwd_pp_kernel(const FwdParams p) {
       sync();
     }
     const bool cp = grp_a ? k + 2 < n_t : k + 3 < n_t;
-    if (cp) issue_tile(grp_a ? (BI + 2) % 4 : (BI + 3) % 4);   // one branch, the copies first
+    if (cp) {                                   // one branch, the copies first
+      issue_tile(grp_a ? (BI + 2) % 4 : (BI + 3) % 4);
+      copies_then_result_wait();
+    } else {
+      mfma_result_wait();
+    }
+    __builtin_amdgcn_sched_barrier(0);
     softmax(k, pass);
     prefetch_v(pre, ic<BI>{});
     __builtin_amdgcn_sched_barrier(0);
@@ -433,7 +445,13 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     // phase 1: A SOFTMAX(0) with its share of tile 2, then V_0's first
     // fragments; B GEMM(-1) = S_0
     if (grp_a) {
-      if (2 < n_t) issue_tile(2);
+      if (2 < n_t) {
+        issue_tile(2);
+        copies_then_result_wait();
+      } else {
+        mfma_result_wait();
+      }
+      __builtin_amdgcn_sched_barrier(0);
       softmax(0, pass);
       prefetch_v(pre, ic<0>{});
     } else {
@@ -446,7 +464,13 @@ void fa_fwd_pp_kernel(const FwdParams p) {
     // opens slot 1 (no barrier before B's GEMM(0)). The pairs k = 1 .. n_t - 1
     // then run from each wave's own point of view, B one phase behind A.
     if (!grp_a) {
-      if (3 < n_t) issue_tile(3);
+      if (3 < n_t) {
+        issue_tile(3);
+        copies_then_result_wait();
+      } else {
+        mfma_result_wait();
+      }
+      __builtin_amdgcn_sched_barrier(0);
       softmax(0, pass);
       prefetch_v(pre, ic<0>{});
     }
