@@ -41,6 +41,8 @@ MAIN = "fwd_b4_h16_n4096_d128"
 # the dQ product only (2d; its S and dP recomputations are not algorithmic).
 # (d = 128 forwards run fa_fwd_pp_kernel, the two-waves-per-SIMD kernel; other d run fa_fwd_kernel)
 FWD_OPTION_TIMINGS = {}
+# The workload on which the dQ options are timed side by side (the causal 8192-token backward).
+DQ_AB_WORKLOAD = "bwd_causal_b2_h16_n8192_d128"
 KERNEL_FLOP_PER_ELEM = {"fa_fwd_pp_kernel": 4, "fa_fwd_kernel": 4, "bwd_dkdv_kernel": 8, "bwd_dq_kernel": 2,
                         "bwd_prep_kernel": 0}
 
@@ -99,7 +101,7 @@ def main():
     import numpy as np
     import torch
 
-    from exact_attention_48_amd import capi, inputs as I
+    from exact_attention_48_amd import capi, inputs as I, probe
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -257,6 +259,17 @@ def main():
                 ent["bwd_ms"] = round(ms_b, 4)
                 ent["bwd_tflops"] = round(flb / (ms_b * 1e-3) / 1e12, 1)
                 ent["bwd_frac_of_peak"] = round(flb / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                if name == DQ_AB_WORKLOAD:
+                    # dQ: the separate pass (what fa_bwd runs) against the fp32 atomic adds a dQ
+                    # accumulated from the dK/dV kernel would need, issued alone
+                    dq_pass = lambda: capi.fa_bwd_ex(qw, kw, vw, ow, lse_w, dow, dqw, dkw, dvw, wl.B, wl.Hq, wl.Hkv,
+                                                     Nw, wl.d, int(wl.causal), wl.scale, cu, wsw, wsb,
+                                                     capi.FA_BWD_DQ, stream)
+                    ent["dq_pass_ms"] = round(time_it(dq_pass, 5), 4)
+                    acc = torch.zeros((wl.B, Nw, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+                    atom = lambda: probe.dq_atomics(acc, wl.B, wl.Hq, Nw, wl.d, int(wl.causal), stream)
+                    ent["dq_fused_atomics_only_ms"] = round(time_it(atom, 5), 4)
+                    del acc
                 del dow, dqw, dkw, dvw, wsw
             workloads[name] = ent
             del qw, kw, vw, ow, lse_w

@@ -1,9 +1,11 @@
-"""Build the HIP library libfa.so in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950.
 
     python -m exact_attention_48_amd.build        # or build() from Python
 
-Every call recompiles. Kernels are compiled with packed FP32 instructions
-disabled (-packed-fp32-ops). Object files go to exact_attention_48_amd/_build/.
+libfa.so is the attention library; libfa_probe.so holds a measurement kernel
+(probe_dq_atomics.hip) that bench.py times beside it. Every call recompiles.
+Kernels are compiled with packed FP32 instructions disabled (-packed-fp32-ops).
+Object files go to exact_attention_48_amd/_build/.
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_bwd.hip", "fa_merge.hip", "fa_exp2.hip"]
+PROBE_SOURCES = ["probe_dq_atomics.hip"]
+PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
 
 
 def hipcc() -> str:
@@ -51,18 +55,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
