@@ -335,6 +335,40 @@ def main():
         del qw, kw, vw, opw, lpw, ow, lw
         torch.cuda.empty_cache()
 
+    # ---------------- library reference points on the same GPU ----------------
+    # What the ROCm libraries reach on this device under the same clock and power
+    # limits: a large bf16 GEMM through torch.mm (hipBLASLt), the practical matrix-core
+    # ceiling, and torch's fused attention (flash backend only, never the math path)
+    # on the two d = 128 forward workloads. Context for the fractions above, not inputs.
+    reference = {}
+    if not args.main_only:
+        M = 8192
+        a_m = torch.randn(M, M, device=dev, dtype=torch.bfloat16)
+        b_m = torch.randn(M, M, device=dev, dtype=torch.bfloat16)
+        ms = time_it(lambda: torch.mm(a_m, b_m), 10)
+        fl = 2.0 * M ** 3
+        reference["torch_mm_bf16_8192"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                           "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del a_m, b_m
+        from torch.nn.attention import sdpa_kernel, SDPBackend
+        import torch.nn.functional as F
+        for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128"):
+            wl = I.WORKLOADS[name]
+            qs = (wl.B, wl.N, wl.Hq, wl.d)
+            qt, kt, vt = (rnd(qs, s).transpose(1, 2) for s in (1, 2, 3))
+            fl = I.counted_flops([wl.N] * wl.B, wl.Hq, wl.d, wl.causal)
+            try:
+                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                    ms = time_it(lambda: F.scaled_dot_product_attention(qt, kt, vt, is_causal=wl.causal,
+                                                                        scale=wl.scale), 5)
+                reference["torch_sdpa_flash_" + name] = {
+                    "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                    "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            except RuntimeError as e:          # no flash kernel for this device in this torch build
+                reference["torch_sdpa_flash_" + name] = {"unavailable": str(e)[:200]}
+            del qt, kt, vt
+        torch.cuda.empty_cache()
+
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -385,6 +419,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "workloads": workloads,
+        "library_reference": reference,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(0),
