@@ -12,6 +12,9 @@ Meant to run under ``rocprofv3 --pmc ...`` (or ``--kernel-trace``):
               scaled N(0,1) draw, descale 1/64)
 --part copy   a plain device-to-device copy of 512 MiB (known byte count, used
               to calibrate FETCH_SIZE / WRITE_SIZE against real HBM bytes)
+--part gemm   torch.mm of two 8192 x 8192 bf16 matrices (the ROCm GEMM library on
+              the same matrix cores: clock and MFMA busy of a plain dense GEMM
+              beside the attention kernels')
 --exp-mode, --tau, --lpt   forward options (fa_fwd_ex) for --part fwd / bwd
 Summaries of the profiler's CSV output: ``python -m exact_attention_48_amd.profile_summary``.
 Inputs are seeded N(0,1) bf16 drawn on the GPU with the workload's shapes.
@@ -30,7 +33,7 @@ from . import capi, inputs as I
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="fwd_b4_h16_n4096_d128", choices=sorted(I.WORKLOADS))
-    ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "split", "fp8", "copy"])
+    ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "split", "fp8", "copy", "gemm"])
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--exp-mode", type=int, default=capi.FA_EXP_HW, choices=[capi.FA_EXP_HW, capi.FA_EXP_POLY])
     ap.add_argument("--tau", type=float, default=32.0)
@@ -44,6 +47,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"copied {src.numel()} bytes x {args.reps}")
+        return
+    if args.part == "gemm":
+        a = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        b = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        for _ in range(args.reps):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
+        print(f"gemm 8192^3 bf16 x {args.reps} done")
         return
     w = I.WORKLOADS[args.workload]
     g = torch.Generator(device=dev)

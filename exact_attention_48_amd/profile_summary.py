@@ -22,7 +22,9 @@ traffic   HBM bytes per launch of one kernel from a FETCH_SIZE and a WRITE_SIZE 
           (KiB per dispatch), each scaled by what the same counter reads for the
           512 MiB device copy of ``profile_run --part copy``; prints the key: value
           file that bench.py reads, with the kernel's current source hash.
-Kernel names are shortened to the function name inside namespace ``fa``.
+Kernel names are shortened to the function name inside namespace ``fa``; other
+kernels (a library's) are kept only when ``--include LABEL=REGEX`` matches their
+name, and are then listed under LABEL.
 """
 from __future__ import annotations
 
@@ -38,9 +40,15 @@ from .kernel_sources import source_hash
 COPY_BYTES = 512 << 20
 
 
+_INCLUDE = []   # (label, compiled regex) for kernels outside namespace fa
+
+
 def _short(name: str):
     m = re.search(r"fa::(\w+)(<[^()]*>)?", name)
     if not m:
+        for label, rx in _INCLUDE:
+            if rx.search(name):
+                return label
         return None
     return m.group(1) + (m.group(2) or "")
 
@@ -159,7 +167,15 @@ def main(argv=None):
     r = sub.add_parser("traffic")
     for n in ("kernel", "workload", "fetch", "write", "copy-fetch", "copy-write"):
         r.add_argument("--" + n, required=True)
+    for p in (t, c):
+        p.add_argument("--include", action="append", default=[], metavar="LABEL=REGEX")
     args = ap.parse_args(argv)
+    _INCLUDE.clear()
+    for spec in getattr(args, "include", []):
+        label, _, rx = spec.partition("=")
+        if not label or not rx:
+            raise SystemExit(f"--include wants LABEL=REGEX, got {spec!r}")
+        _INCLUDE.append((label, re.compile(rx)))
     {"trace": trace, "counters": counters, "traffic": traffic}[args.cmd](args)
 
 

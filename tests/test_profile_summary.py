@@ -99,3 +99,18 @@ def test_source_hash_is_stable(kernel):
     h = kernel_sources.source_hash(kernel)
     assert len(h) == 16 and int(h, 16) >= 0
     assert h == kernel_sources.source_hash(kernel)
+
+
+def test_library_kernels_only_when_included(tmp_path):
+    lib = "Cijk_Alik_Bljk_BBS_BH_MT256x256x64_MI16x16x1"
+    rows = [{"Kernel_Name": lib, "Start_Timestamp": 0, "End_Timestamp": 800_000},
+            {"Kernel_Name": FWD, "Start_Timestamp": 0, "End_Timestamp": 400_000}]
+    p = tmp_path / "g_kernel_trace.csv"
+    _write(p, TRACE_COLS, rows)
+    assert "Cijk" not in _run(["trace", "--csv", str(p)])
+    out = _run(["trace", "--csv", str(p), "--include", "gemm_bf16=^Cijk_"])
+    line = [l for l in out.splitlines() if l.startswith("| `gemm_bf16`")][0]
+    assert "| 1 | 800.0 |" in line
+    assert "fa_fwd_pp_kernel" in out
+    with pytest.raises(SystemExit):
+        _run(["trace", "--csv", str(p), "--include", "no-regex"])
