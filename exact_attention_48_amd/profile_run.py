@@ -16,13 +16,23 @@ Meant to run under ``rocprofv3 --pmc ...`` (or ``--kernel-trace``):
               the same matrix cores: clock and MFMA busy of a plain dense GEMM
               beside the attention kernels')
 --exp-mode, --tau, --lpt   forward options (fa_fwd_ex) for --part fwd / bwd
+--seconds S   launch back to back for S seconds instead of --reps times, and print
+              the host-clock time per call
+--power       with --seconds: read socket power and the XCDs' gfx clocks from
+              ``amd-smi metric`` while the launches run, and print their medians
+              (readings of the first second, the clock ramp, are dropped)
 Summaries of the profiler's CSV output: ``python -m exact_attention_48_amd.profile_summary``.
 Inputs are seeded N(0,1) bf16 drawn on the GPU with the workload's shapes.
 """
 from __future__ import annotations
 
 import argparse
+import json
 import math
+import re
+import subprocess
+import threading
+import time
 
 import numpy as np
 import torch
@@ -30,11 +40,84 @@ import torch
 from . import capi, inputs as I
 
 
+def parse_smi_metrics(text: str):
+    """(socket power in W, mean gfx clock of the XCDs in MHz) from the JSON of
+    ``amd-smi metric --power --clock --json``; None where a reading is missing."""
+    vals = []
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            if "value" in x and "unit" in x:
+                vals.append(("/".join(path), x["value"]))
+                return
+            for k, v in x.items():
+                walk(v, path + [str(k)])
+        elif isinstance(x, list):
+            for i, v in enumerate(x):
+                walk(v, path + [str(i)])
+    walk(json.loads(text), [])
+    pw = [v for k, v in vals if k.endswith("/socket_power") and isinstance(v, (int, float))]
+    ck = [v for k, v in vals if re.search(r"/gfx_\d+/clk$", k) and isinstance(v, (int, float))]
+    return (float(pw[0]) if pw else None), (sum(ck) / len(ck) if ck else None)
+
+
+def _power_sampler(stop, samples):
+    while not stop.is_set():
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True, text=True,
+                               timeout=10)
+            pw, ck = parse_smi_metrics(r.stdout)
+        except (OSError, ValueError, subprocess.SubprocessError):
+            continue
+        if pw is not None and ck is not None:
+            samples.append((time.time(), pw, ck))
+
+
+def _run(launch, args, label):
+    if args.seconds <= 0:
+        for _ in range(args.reps):
+            launch()
+        torch.cuda.synchronize()
+        print(f"{label} x {args.reps} done")
+        return
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    stop, samples = threading.Event(), []
+    th = threading.Thread(target=_power_sampler, args=(stop, samples)) if args.power else None
+    t0 = time.time()
+    if th:
+        th.start()
+    n = 0
+    while time.time() - t0 < args.seconds:
+        for _ in range(4):
+            launch()
+        n += 4
+        torch.cuda.synchronize()
+    el = time.time() - t0
+    if th:
+        stop.set()
+        th.join()
+    print(f"{label}: {n} calls in {el:.2f} s, {1e3 * el / n:.4f} ms per call (host clock)")
+    if args.power:
+        late = [x for x in samples if x[0] - t0 >= 1.0]     # past the first second's ramp
+        if not late:
+            print("power: no amd-smi readings")
+            return
+        pw = sorted(x[1] for x in late)
+        ck = sorted(x[2] for x in late)
+        print(f"power: {len(late)} readings after the first second; socket power median {pw[len(pw) // 2]:.0f} W "
+              f"(min {pw[0]:.0f}, max {pw[-1]:.0f}); gfx clock, mean of the XCDs, median {ck[len(ck) // 2]:.0f} MHz "
+              f"(min {ck[0]:.0f}, max {ck[-1]:.0f})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="fwd_b4_h16_n4096_d128", choices=sorted(I.WORKLOADS))
     ap.add_argument("--part", default="fwd", choices=["fwd", "bwd", "split", "fp8", "copy", "gemm"])
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--seconds", type=float, default=0.0, help="run back to back for this long instead of --reps")
+    ap.add_argument("--power", action="store_true", help="with --seconds: sample amd-smi power and clocks")
     ap.add_argument("--exp-mode", type=int, default=capi.FA_EXP_HW, choices=[capi.FA_EXP_HW, capi.FA_EXP_POLY])
     ap.add_argument("--tau", type=float, default=32.0)
     ap.add_argument("--lpt", type=int, default=1, choices=[0, 1])
@@ -43,18 +126,12 @@ def main():
     if args.part == "copy":
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(args.reps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"copied {src.numel()} bytes x {args.reps}")
+        _run(lambda: dst.copy_(src), args, f"copy of {src.numel()} bytes")
         return
     if args.part == "gemm":
         a = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
         b = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
-        for _ in range(args.reps):
-            torch.mm(a, b)
-        torch.cuda.synchronize()
-        print(f"gemm 8192^3 bf16 x {args.reps} done")
+        _run(lambda: torch.mm(a, b), args, "gemm 8192^3 bf16")
         return
     w = I.WORKLOADS[args.workload]
     g = torch.Generator(device=dev)
@@ -69,11 +146,11 @@ def main():
         lp = torch.empty((w.n_splits, w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
         o = torch.empty((w.B, w.N, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-        for _ in range(args.reps):
+
+        def split_merge():
             capi.fa_fwd_split(q, k, v, op, lp, w.B, w.Hq, w.Hkv, w.N, w.Nk, w.d, int(w.causal), w.scale, w.n_splits)
             capi.fa_merge(op, lp, o, lse, w.n_splits, w.B, w.Hq, w.N, w.d)
-        torch.cuda.synchronize()
-        print(f"split x {args.reps} on {args.workload} done")
+        _run(split_merge, args, f"split on {args.workload}")
         return
     if args.part == "fp8":
         if w.kind != "fp8":
@@ -85,10 +162,8 @@ def main():
         kd = torch.full((w.B, w.Hkv), 1.0 / 64, dtype=torch.float32, device=dev)
         o = torch.empty((w.B, w.N, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
-        for _ in range(args.reps):
-            capi.fa_fwd_fp8(q8, k8, v, qd, kd, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale)
-        torch.cuda.synchronize()
-        print(f"fp8 x {args.reps} on {args.workload} done")
+        _run(lambda: capi.fa_fwd_fp8(q8, k8, v, qd, kd, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale),
+             args, f"fp8 on {args.workload}")
         return
     if w.varlen:
         lens = I.draw_lengths(np.random.default_rng(w.seed), w.B, w.len_lo, w.len_hi)
@@ -107,19 +182,15 @@ def main():
     opt = capi.FaOptions(args.exp_mode, args.tau, args.lpt)
     fwd = lambda: capi.fa_fwd_ex(q, k, v, o, lse, w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), w.scale, cu, opt)
     if args.part == "fwd":
-        for _ in range(args.reps):
-            fwd()
-    else:
-        fwd()
-        do = rnd(qs)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        nb = capi.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), int(w.varlen))
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        for _ in range(args.reps):
-            capi.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), w.scale, cu,
-                        ws, nb)
-    torch.cuda.synchronize()
-    print(f"{args.part} x {args.reps} on {args.workload} done")
+        _run(fwd, args, f"fwd on {args.workload}")
+        return
+    fwd()
+    do = rnd(qs)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nb = capi.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), int(w.varlen))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _run(lambda: capi.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.B, w.Hq, w.Hkv, N, w.d, int(w.causal), w.scale, cu,
+                             ws, nb), args, f"bwd on {args.workload}")
 
 
 if __name__ == "__main__":
