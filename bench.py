@@ -64,7 +64,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)   # ~0.45 s: the clock settles before the timed steps
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-workload figures")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = auto)")
@@ -194,13 +194,20 @@ def main():
             g.manual_seed(seed)
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-        def time_it(fn, reps):
-            # three warm calls, then the median of three timed windows
-            for _ in range(3):
+        def time_it(fn, reps, warm_s=1.0):
+            # Steady state: back-to-back calls for warm_s seconds first (after an idle gap the
+            # clock takes about a second to settle: the first window runs ~10 % slow and the
+            # next ones 1.5-2.5 % slow), then the median of five timed windows.
+            t0 = time.perf_counter()
+            n = 0
+            while n < 3 or time.perf_counter() - t0 < warm_s:
                 fn()
+                n += 1
+                if n % 8 == 0:
+                    torch.cuda.synchronize()
             torch.cuda.synchronize()
             windows = []
-            for _ in range(3):
+            for _ in range(5):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 for _ in range(reps):
@@ -208,7 +215,7 @@ def main():
                 b.record(stream)
                 torch.cuda.synchronize()
                 windows.append(a.elapsed_time(b) / reps)
-            return sorted(windows)[1]
+            return sorted(windows)[2]
 
         for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
                      "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64",
