@@ -16,6 +16,9 @@ Meant to run under ``rocprofv3 --pmc ...`` (or ``--kernel-trace``):
               the same matrix cores: clock and MFMA busy of a plain dense GEMM
               beside the attention kernels')
 --exp-mode, --tau, --lpt   forward options (fa_fwd_ex) for --part fwd / bwd
+--warm-seconds W   first launch back to back for W seconds, so that the clock has
+              settled before the calls that count (select those in a trace with
+              ``profile_summary trace --last N``)
 --seconds S   launch back to back for S seconds instead of --reps times, and print
               the host-clock time per call
 --power       with --seconds: read socket power and the XCDs' gfx clocks from
@@ -74,6 +77,16 @@ def _power_sampler(stop, samples):
 
 
 def _run(launch, args, label):
+    if args.warm_seconds > 0:                       # the clock settles over about a second of load
+        t0 = time.time()
+        n = 0
+        while time.time() - t0 < args.warm_seconds:
+            launch()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        print(f"{label}: {n} warm-up calls")
     if args.seconds <= 0:
         for _ in range(args.reps):
             launch()
@@ -118,6 +131,8 @@ def main():
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--seconds", type=float, default=0.0, help="run back to back for this long instead of --reps")
     ap.add_argument("--power", action="store_true", help="with --seconds: sample amd-smi power and clocks")
+    ap.add_argument("--warm-seconds", type=float, default=0.0,
+                    help="launch back to back for this long first (untimed; a trace keeps them: see trace --last)")
     ap.add_argument("--exp-mode", type=int, default=capi.FA_EXP_HW, choices=[capi.FA_EXP_HW, capi.FA_EXP_POLY])
     ap.add_argument("--tau", type=float, default=32.0)
     ap.add_argument("--lpt", type=int, default=1, choices=[0, 1])

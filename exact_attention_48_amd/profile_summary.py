@@ -8,7 +8,8 @@
 
 trace     per-kernel call count, mean / median / min / max duration (us) from a
           ``--kernel-trace`` CSV; ``--skip N`` drops the first N dispatches of every
-          kernel (the cold ones) so that the figures describe warm calls.
+          kernel (the cold ones) so that the figures describe warm calls, ``--last N``
+          keeps only the last N (the calls after a warm-up of any length).
 counters  per-kernel means over the profiled dispatches of ``--pmc`` CSVs (several
           passes may be given, one per file), with derived figures:
           cycles = GRBM_GUI_ACTIVE / 8 (it is summed over the 8 XCDs), clock =
@@ -69,10 +70,14 @@ def trace(args):
     print("|---|---|---|---|---|---|")
     for k, v in durs.items():
         w = v[args.skip:] if len(v) > args.skip else v
+        if args.last:
+            w = w[-args.last:]
         print(f"| `{k}` | {len(w)} | {statistics.mean(w):.1f} | {statistics.median(w):.1f} | {min(w):.1f} | "
               f"{max(w):.1f} |")
     if args.skip:
         print(f"\n(first {args.skip} dispatch(es) of each kernel dropped)")
+    if args.last:
+        print(f"\n(the last {args.last} dispatch(es) of each kernel)")
 
 
 def _counter_means(paths):
@@ -162,6 +167,7 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("--csv", required=True)
     t.add_argument("--skip", type=int, default=0)
+    t.add_argument("--last", type=int, default=0, help="keep only the last N dispatches of each kernel")
     c = sub.add_parser("counters")
     c.add_argument("--csv", action="append", required=True)
     r = sub.add_parser("traffic")

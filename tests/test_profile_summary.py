@@ -114,3 +114,15 @@ def test_library_kernels_only_when_included(tmp_path):
     assert "fa_fwd_pp_kernel" in out
     with pytest.raises(SystemExit):
         _run(["trace", "--csv", str(p), "--include", "no-regex"])
+
+
+def test_trace_last_keeps_the_final_calls(tmp_path):
+    rows = []
+    t = 0
+    for us in (900, 800, 700, 100, 110, 120):
+        rows.append({"Kernel_Name": FWD, "Start_Timestamp": t, "End_Timestamp": t + us * 1000})
+        t += 10 ** 7
+    p = tmp_path / "w_kernel_trace.csv"
+    _write(p, TRACE_COLS, rows)
+    line = [l for l in _run(["trace", "--csv", str(p), "--last", "3"]).splitlines() if "fa_fwd_pp_kernel" in l][0]
+    assert [c.strip() for c in line.strip("|").split("|")][1:] == ["3", "110.0", "110.0", "100.0", "120.0"]
