@@ -20,6 +20,9 @@ struct Problem {
 // Limits of this implementation.
 constexpr long kMaxItems = 1L << 24;        // query tiles x heads x sequences per launch
 constexpr long kMaxTokens = 1L << 31;       // tokens per tensor (B * N, or T)
+// K/V row elements (Hkv * d): the d = 128 forward addresses 256 key tiles of a
+// head from one buffer descriptor, whose offsets must stay below 2^31 bytes.
+constexpr long kMaxKvRow = 1L << 15;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -34,6 +37,7 @@ inline fa_status check_problem(const Problem& pr, float scale) {
   if (!(scale >= 0.0f) || scale > 3.0e38f) return FA_ERR_INVALID_ARGUMENT;
   if (pr.d != 64 && pr.d != 128) return FA_ERR_UNSUPPORTED;
   if (pr.B * pr.N > kMaxTokens) return FA_ERR_UNSUPPORTED;
+  if (pr.Hkv * pr.d > kMaxKvRow) return FA_ERR_UNSUPPORTED;
   const long tiles = (pr.N + 127) / 128;
   if (pr.B * pr.Hq * tiles > kMaxItems) return FA_ERR_UNSUPPORTED;
   return FA_OK;

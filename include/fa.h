@@ -37,6 +37,9 @@
  *  - All arguments are validated on the host before anything is launched; an
  *    invalid argument returns a status code and enqueues nothing.
  *  - Supported head sizes: d = 64 and d = 128.
+ *  - Size limits (beyond them a call returns FA_ERR_UNSUPPORTED): at most 2^31
+ *    tokens per tensor (B * N, or T), at most 2^24 work items
+ *    (B * Hq * ceil(N / 128)), and Hkv * d <= 32768 (Hkv <= 256 at d = 128).
  *  - Entry points are stateless and may be called concurrently from several
  *    host threads.
  */
@@ -54,7 +57,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned pointer, Hq % Hkv != 0, scale not
                                     finite or negative */
-    FA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head size other than 64 or 128) */
+    FA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head size other than 64 or 128,
+                                    sizes beyond the limits below) */
     FA_ERR_WORKSPACE = 3,        /* backward workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
 } fa_status;

@@ -69,6 +69,9 @@ def fwd(*, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=128, causal=0, s
     (dict(lse=A + 2), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(cu=A + 1), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(B=1 << 20, N=1 << 20), capi.FA_ERR_UNSUPPORTED),
+    (dict(Hq=257, Hkv=257), capi.FA_ERR_UNSUPPORTED),        # Hkv * d > 32768
+    (dict(Hq=513, Hkv=513, d=64), capi.FA_ERR_UNSUPPORTED),
+    (dict(Hq=256, Hkv=256, q=None), capi.FA_ERR_INVALID_ARGUMENT),   # at the limit: the pointer check decides
     (dict(opt=capi.FaOptions(7, 8.0, 1)), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(opt=capi.FaOptions(0, -1.0, 1)), capi.FA_ERR_INVALID_ARGUMENT),
     (dict(opt=capi.FaOptions(0, 8.0, 2)), capi.FA_ERR_INVALID_ARGUMENT),

@@ -1,7 +1,8 @@
 """Forward parity on uniform d = 128 batches with more work items (query tiles of
 256 rows) than the GPU has CUs, so that every CU runs several of them one after
-another: 288-320 items with GQA, causal and non-causal masks, ragged sequence
-ends and the conditional-rescale re-run. Rows checked: the first and last of
+another: 288-768 items with GQA, causal and non-causal masks, ragged sequence
+ends, the widest K/V rows the library takes (256 heads of d = 128) and the
+conditional-rescale re-run. Rows checked: the first and last of
 every wave's 32 rows in every 256-row tile, plus a stride through the rest.
 """
 import numpy as np
@@ -29,6 +30,7 @@ CASES = [
     (2, 1000, 40, 10, True),    # 4, 8, 12, 16
     (3, 700, 32, 8, False),     # 11
     (3, 700, 32, 32, True),     # 4, 8, 11
+    (1, 700, 256, 256, True),   # the widest K/V rows the library takes (Hkv * d = 32768)
 ]
 
 
