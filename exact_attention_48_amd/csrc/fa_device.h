@@ -188,8 +188,6 @@ __device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t rsrc, unsigned v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 4, (int)voffset, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // s_waitcnt immediate: at most `vm` vector-memory operations (which include the
 // HBM->LDS copies) and no LDS operation of this wave outstanding.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
