@@ -2,8 +2,8 @@
 //
 // The backward pass recomputes the softmax from the forward's log-sum-exp and
 // produces dQ, dK and dV (backward pass: abstract on the zhuanzhiai.com page;
-// the pages' own design uses tensor memory and 2-CTA MMA to cut shared-memory
-// traffic and atomic adds there, which this hardware does not have). With
+// there the pages lean on tensor memory and 2-CTA MMA, which this hardware
+// lacks, so that fewer bytes cross shared memory and fewer atomics run). With
 // P = exp(S - LSE) and D_i = dO_i . O_i:
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //

@@ -2,9 +2,9 @@
 // waves per SIMD that take turns on the matrix core.
 //
 // The pages overlap the softmax of one tile with the matrix products of
-// another through a ping-pong of two groups of warps ("ping-pong pipeline that
-// overlaps MMA with softmax", daily.dev "Summary" of the Together AI post;
-// co-design list of the phantomic12 summary). On gfx950 a wave issues at most
+// another by alternating two groups of warps between the two kinds of work
+// (daily.dev "Summary" of the Together AI post; co-design list of the
+// phantomic12 summary). On gfx950 a wave issues at most
 // one instruction at a time, so one wave per SIMD that interleaves its own
 // MFMAs with its own softmax arithmetic leaves the matrix core idle while the
 // vector instructions issue. With two waves per SIMD, one wave's MFMAs run

@@ -126,3 +126,13 @@ def test_trace_last_keeps_the_final_calls(tmp_path):
     _write(p, TRACE_COLS, rows)
     line = [l for l in _run(["trace", "--csv", str(p), "--last", "3"]).splitlines() if "fa_fwd_pp_kernel" in l][0]
     assert [c.strip() for c in line.strip("|").split("|")][1:] == ["3", "110.0", "110.0", "100.0", "120.0"]
+
+
+def test_code_only_ignores_comments_not_code():
+    a = 'int f(int x) { // add one\n  return x + 1; /* done */ }\nconst char* s = "a // b";\n'
+    b = 'int f(int x) {\n\n  return x + 1;   }\n// a comment\nconst char* s = "a // b";'
+    assert kernel_sources.code_only(a) == kernel_sources.code_only(b)
+    assert "a // b" in kernel_sources.code_only(a)              # inside a string: code
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "a // b";'
+    assert kernel_sources.code_only(a) != kernel_sources.code_only(c)
+    assert kernel_sources.code_only("x = '\\'';  // q") == "x = '\\'';"
