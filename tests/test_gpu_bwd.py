@@ -63,6 +63,19 @@ def test_backward_small(case):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_backward_zero_scale(causal):
+    """softmax_scale = 0: P is uniform over the visible keys, so dV = P^T dO is a
+    running mean of dO, while dQ = scale dS K and dK = scale dS^T Q vanish exactly."""
+    x = I.make_inputs(2, 300, 4, 2, 128, causal, seed=63, scale=0.0, with_do=True)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(x)
+    rq, rk, rv = oracle.attention_backward(H.f64(x.q), H.f64(x.k), H.f64(x.v), H.f64(x.do), x.scale, x.causal)
+    assert not np.any(rq) and not np.any(rk)
+    assert torch.count_nonzero(dq).item() == 0 and torch.count_nonzero(dk).item() == 0, "dQ and dK must be exactly 0"
+    e = H.rel_fro(H.host_f64(dv), rv)
+    assert e <= H.GRAD_REL_FRO, f"dV relative Frobenius error {e:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_varlen_gqa(causal, d):
     lens = [1, 130, 0, 257, 64, 7, 200]

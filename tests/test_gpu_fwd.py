@@ -221,3 +221,12 @@ def test_zero_scale_gives_uniform_weights(d, causal):
     H.check_forward(o, lse, o_ref, lse_ref, f"scale 0 d={d} causal={causal}")
     n_vis = np.arange(1, 301) if causal else np.full(300, 300)
     np.testing.assert_allclose(H.host_f64(lse)[0, 0], np.log(n_vis), atol=1e-3)
+    # the packed layout with grouped heads, empty and one-token sequences
+    x = I.make_inputs(0, 0, 4, 2, d, causal, seed=62, scale=0.0, lengths=np.array([1, 257, 0, 64]))
+    o_ref, lse_ref = H.oracle_forward(x)
+    *_, o, lse = H.gpu_forward(x)
+    H.check_forward(o, lse, o_ref, lse_ref, f"scale 0 packed d={d} causal={causal}")
+    lse_h = H.host_f64(lse)
+    for a, b in zip(x.cu_seqlens[:-1], x.cu_seqlens[1:]):
+        n_vis = np.arange(1, b - a + 1) if causal else np.full(b - a, b - a)
+        np.testing.assert_allclose(lse_h[:, a:b], np.broadcast_to(np.log(n_vis), (4, b - a)), atol=1e-3)
