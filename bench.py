@@ -60,6 +60,90 @@ def _fwd_option_timings():
             "fwd_causal_varlen16_hq32_hkv8_d128": [lpt0]}
 
 
+def steady_ms(fn, reps, stream, warm_s=1.0):
+    """Milliseconds per call in steady state: back-to-back calls for warm_s seconds first
+    (after an idle gap the clock takes about a second to settle: the first window runs
+    ~10 % slow and the next ones 1.5-2.5 % slow), then the median of five timed windows
+    of `reps` calls, timed with HIP events on `stream`."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    windows = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        windows.append(a.elapsed_time(b) / reps)
+    return sorted(windows)[2]
+
+
+def library_reference():
+    """What the ROCm libraries reach on this device under the same clock and power
+    limits: a large bf16 GEMM through torch.mm (hipBLASLt), the practical matrix-core
+    ceiling, and torch's fused attention (flash backend only, never the math path) on
+    the two d = 128 forward workloads. Context for the kernels' fractions, not inputs.
+    Runs in a child process of the benchmark, so that a failure here cannot cost the
+    benchmark its own line."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    from exact_attention_48_amd import inputs as I
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev)
+    out = {}
+    M = 8192
+    g.manual_seed(1)
+    a_m = torch.randn(M, M, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b_m = torch.randn(M, M, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ms = steady_ms(lambda: torch.mm(a_m, b_m), 10, stream)
+    fl = 2.0 * M ** 3
+    out["torch_mm_bf16_8192"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                 "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del a_m, b_m
+    for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128"):
+        wl = I.WORKLOADS[name]
+        qs = (wl.B, wl.N, wl.Hq, wl.d)
+        g.manual_seed(2)
+        qt, kt, vt = (torch.randn(qs, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16).transpose(1, 2)
+                      for _ in range(3))
+        fl = I.counted_flops([wl.N] * wl.B, wl.Hq, wl.d, wl.causal)
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                ms = steady_ms(lambda: F.scaled_dot_product_attention(qt, kt, vt, is_causal=wl.causal,
+                                                                      scale=wl.scale), 5, stream)
+            out["torch_sdpa_flash_" + name] = {
+                "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        except RuntimeError as e:          # no flash kernel for this device in this torch build
+            out["torch_sdpa_flash_" + name] = {"unavailable": str(e)[:200]}
+        del qt, kt, vt
+    return out
+
+
+def _library_reference_child():
+    """The library reference block from a child process (bench.py --library-reference)."""
+    import subprocess
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--library-reference"], capture_output=True,
+                           text=True, timeout=240)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            return {"unavailable": f"child exited with status {r.returncode}: {r.stderr.strip()[-200:]}"}
+        return json.loads(lines[-1])
+    except (subprocess.SubprocessError, OSError, ValueError) as e:
+        return {"unavailable": repr(e)[:200]}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,6 +152,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-workload figures")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = auto)")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="print only the ROCm library reference figures (one JSON object) and exit")
     return ap.parse_args()
 
 
@@ -93,6 +179,9 @@ def read_traffic(kernel, workload):
 
 def main():
     args = parse()
+    if args.library_reference:
+        print(json.dumps(library_reference()))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -194,28 +283,8 @@ def main():
             g.manual_seed(seed)
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-        def time_it(fn, reps, warm_s=1.0):
-            # Steady state: back-to-back calls for warm_s seconds first (after an idle gap the
-            # clock takes about a second to settle: the first window runs ~10 % slow and the
-            # next ones 1.5-2.5 % slow), then the median of five timed windows.
-            t0 = time.perf_counter()
-            n = 0
-            while n < 3 or time.perf_counter() - t0 < warm_s:
-                fn()
-                n += 1
-                if n % 8 == 0:
-                    torch.cuda.synchronize()
-            torch.cuda.synchronize()
-            windows = []
-            for _ in range(5):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(reps):
-                    fn()
-                b.record(stream)
-                torch.cuda.synchronize()
-                windows.append(a.elapsed_time(b) / reps)
-            return sorted(windows)[2]
+        def time_it(fn, reps):
+            return steady_ms(fn, reps, stream)
 
         for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128",
                      "fwd_causal_varlen16_hq32_hkv8_d128", "bwd_causal_b2_h16_n8192_d128", "fwd_b1_h2_n256_d64",
@@ -342,39 +411,8 @@ def main():
         del qw, kw, vw, opw, lpw, ow, lw
         torch.cuda.empty_cache()
 
-    # ---------------- library reference points on the same GPU ----------------
-    # What the ROCm libraries reach on this device under the same clock and power
-    # limits: a large bf16 GEMM through torch.mm (hipBLASLt), the practical matrix-core
-    # ceiling, and torch's fused attention (flash backend only, never the math path)
-    # on the two d = 128 forward workloads. Context for the fractions above, not inputs.
-    reference = {}
-    if not args.main_only:
-        M = 8192
-        a_m = torch.randn(M, M, device=dev, dtype=torch.bfloat16)
-        b_m = torch.randn(M, M, device=dev, dtype=torch.bfloat16)
-        ms = time_it(lambda: torch.mm(a_m, b_m), 10)
-        fl = 2.0 * M ** 3
-        reference["torch_mm_bf16_8192"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                                           "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del a_m, b_m
-        from torch.nn.attention import sdpa_kernel, SDPBackend
-        import torch.nn.functional as F
-        for name in ("fwd_b4_h16_n4096_d128", "fwd_causal_b2_h16_n16384_d128"):
-            wl = I.WORKLOADS[name]
-            qs = (wl.B, wl.N, wl.Hq, wl.d)
-            qt, kt, vt = (rnd(qs, s).transpose(1, 2) for s in (1, 2, 3))
-            fl = I.counted_flops([wl.N] * wl.B, wl.Hq, wl.d, wl.causal)
-            try:
-                with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-                    ms = time_it(lambda: F.scaled_dot_product_attention(qt, kt, vt, is_causal=wl.causal,
-                                                                        scale=wl.scale), 5)
-                reference["torch_sdpa_flash_" + name] = {
-                    "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                    "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            except RuntimeError as e:          # no flash kernel for this device in this torch build
-                reference["torch_sdpa_flash_" + name] = {"unavailable": str(e)[:200]}
-            del qt, kt, vt
-        torch.cuda.empty_cache()
+    # ---------------- library reference points (child process) ----------------
+    reference = None if args.main_only else _library_reference_child()
 
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
