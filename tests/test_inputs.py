@@ -72,3 +72,16 @@ def test_e4m3_encoder_round_trips_and_rounds_to_even():
     # halfway cases go to the even code; beyond 448 saturates
     got = I.f32_to_e4m3_bits(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 500.0, -1e9, np.nan]))
     assert got.tolist() == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0xFE, 0x7F]
+
+
+def test_bf16_ulp_is_the_spacing_of_bf16_values():
+    """The O gate's ulp (tests/gpu_helpers.py) against the bf16 grid itself: the
+    distance from a bf16 value to the next one up."""
+    from tests import gpu_helpers as H
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(4000) * np.exp2(rng.integers(-6, 6, 4000))
+    bits = I.f32_to_bf16_bits(x.astype(np.float32))
+    v = I.bf16_bits_to_f64(bits)
+    up = I.bf16_bits_to_f64((bits.astype(np.uint32) + 1).astype(np.uint16))
+    np.testing.assert_array_equal(np.abs(up - v), H.bf16_ulp(v))
+    assert H.o_bound(np.array([0.5, 1.99, 2.0, 3.9, 4.0]))[[0, 1, 2, 4]].tolist() == [1e-2, 1e-2, 2 ** -6, 2 ** -5]
