@@ -148,7 +148,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=200)   # ~0.45 s: the clock settles before the timed steps
+    ap.add_argument("--warmup", type=int, default=500)   # ~1 s: the clock settles before the timed steps
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-workload figures")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = auto)")
